@@ -1,0 +1,324 @@
+"""Benchmark of the paged KV attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-flush]
+                    [--keys-per-split S] [--cpu-seconds T]
+
+Headline workload (decode-b256): 256 requests, 16 query / 8 KV heads,
+head_dim 128, page_size 256, contexts U[16,1024] + U[0,1024], bf16.  One step
+is the hot path over one batch: the scatter write of the 256 new tokens,
+then paged decode.  ``value`` is the step's algorithmic HBM bytes (every K/V
+row of every context read once, q read, output and new rows written) per
+second.  A second leg times the varlen prefill workload (8 requests, cached
+prefix U[0,512] + chunk U[32,2048], page 16): its step is the chunk write
+then prefill, reported as causal TFLOP/s.
+
+Inputs are seeded synthetic data put in HBM before timing.  Before every
+timed step a 512 MiB buffer is written so the 256 MB Infinity Cache holds
+nothing of the inputs.  Each step is bracketed by HIP events on the stream
+the kernels run on; the roofline figure divides the decode call's
+algorithmic bytes by its own event-timed duration.  The CPU baseline runs the
+fp64 oracle (as is) on a bounded sample of the same workload on the host.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import resource
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+METRIC = "paged-decode attn GB/s (% of HBM peak) @B=256; prefill attn TFLOP/s (% MFMA)"
+FLUSH_BYTES = 512 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--keys-per-split", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--skip-prefill", action="store_true")
+    ap.add_argument("--skip-cpu", action="store_true")
+    return ap.parse_args()
+
+
+# ---- device inputs (workload bits -> tensors, written through the library) ---
+def _to_dev(bits, dev):
+    import torch
+    arr = np.ascontiguousarray(bits)
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(arr.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(arr.view(np.int32)).to(dev).view(torch.float32)
+
+
+def _i32(a, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+
+def _pools(w, dev):
+    import torch
+    shape = (w.num_pages, w.num_kv_heads, w.page_size, w.head_dim)
+    raw = torch.full(shape, 0x7FC0, dtype=torch.int16, device=dev)
+    return raw.view(torch.bfloat16), raw.clone().view(torch.bfloat16)
+
+
+class Inputs:
+    def __init__(self, w, dev):
+        import paged_kv_attention_16_amd as qil
+        d = w.gather()
+        self.kp, self.vp = _pools(w, dev)
+        qil.kv_write(_to_dev(d["k_cached"], dev), _to_dev(d["v_cached"], dev), self.kp, self.vp,
+                     _i32(d["cached_slots"], dev))
+        self.k_new = _to_dev(d["k_new"], dev)
+        self.v_new = _to_dev(d["v_new"], dev)
+        self.q = _to_dev(d["q"], dev)
+        self.slots = _i32(d["new_slots"], dev)
+        self.bt = _i32(w.block_tables, dev)
+        self.ctx = _i32(w.context_lens, dev)
+        self.out = self.q.new_empty(self.q.shape)
+        del d
+
+
+def gpu_legs(args):
+    import torch
+    import paged_kv_attention_16_amd as qil
+    from workloads import make_workload
+
+    if not os.path.exists(qil.lib_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    res = {}
+
+    # ---- decode leg ------------------------------------------------------
+    w = make_workload(3)
+    t0 = time.time()
+    x = Inputs(w, dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+    max_l = int(w.context_lens.max())
+    need = qil.paged_decode_workspace_size(w.batch, w.num_q_heads, w.num_kv_heads, max_l,
+                                           w.page_size, args.keys_per_split)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def write():
+        qil.kv_write(x.k_new, x.v_new, x.kp, x.vp, x.slots, stream=stream)
+
+    def decode():
+        qil.paged_decode(x.out, x.q, x.kp, x.vp, x.bt, x.ctx, max_l, float(w.scale),
+                         keys_per_split=args.keys_per_split, workspace=ws, stream=stream)
+
+    kv_bytes = w.decode_kv_bytes()
+    write_bytes = int(w.new_lens.sum()) * w.num_kv_heads * w.head_dim * 2 * 2 * 2 + 4 * w.batch
+    step_bytes = kv_bytes + w.decode_io_bytes() + write_bytes
+    dec_bytes = kv_bytes + w.decode_io_bytes()
+
+    for _ in range(args.warmup):
+        write(); decode()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush.fill_(float(i))
+        a, b, c = ev[i]
+        a.record(stream)
+        write()
+        b.record(stream)
+        decode()
+        c.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = np.array([a.elapsed_time(c) for a, b, c in ev])
+    dec_ms = np.array([b.elapsed_time(c) for a, b, c in ev])
+    res["decode"] = dict(
+        workload=w, step_ms=float(step_ms.mean()), dec_ms=float(dec_ms.mean()),
+        dec_ms_median=float(np.median(dec_ms)), dec_ms_p10=float(np.percentile(dec_ms, 10)),
+        dec_ms_p90=float(np.percentile(dec_ms, 90)), step_bytes=step_bytes, dec_bytes=dec_bytes,
+        kv_bytes=kv_bytes, wall_s=wall, setup_s=setup_s, workspace=need)
+    print(f"[bench] decode-b256: step {step_ms.mean()*1e3:.1f} us, decode {dec_ms.mean()*1e3:.1f} us "
+          f"({dec_bytes / (dec_ms.mean() * 1e-3) / 1e9:.0f} GB/s), setup {setup_s:.1f}s", flush=True)
+    del x, ws
+    torch.cuda.empty_cache()
+
+    # ---- prefill leg -----------------------------------------------------
+    if not args.skip_prefill:
+        w4 = make_workload(4)
+        x = Inputs(w4, dev)
+        cu = _i32(w4.cu_seqlens(np.arange(w4.batch)), dev)
+        maxq, maxk = int(w4.new_lens.max()), int(w4.context_lens.max())
+
+        def write4():
+            qil.kv_write(x.k_new, x.v_new, x.kp, x.vp, x.slots, stream=stream)
+
+        def prefill():
+            qil.paged_prefill(x.out, x.q, x.kp, x.vp, x.bt, cu, x.ctx, maxq, maxk,
+                              float(w4.scale), stream=stream)
+
+        for _ in range(args.warmup):
+            write4(); prefill()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i in range(args.steps):
+            if not args.no_flush:
+                flush.fill_(float(i))
+            a, b, c = ev[i]
+            a.record(stream)
+            write4()
+            b.record(stream)
+            prefill()
+            c.record(stream)
+        torch.cuda.synchronize()
+        pre_ms = np.array([b.elapsed_time(c) for a, b, c in ev])
+        st_ms = np.array([a.elapsed_time(c) for a, b, c in ev])
+        flops = w4.prefill_flops()
+        res["prefill"] = dict(workload=w4, pre_ms=float(pre_ms.mean()),
+                              pre_ms_median=float(np.median(pre_ms)), step_ms=float(st_ms.mean()),
+                              flops=flops)
+        print(f"[bench] prefill-varlen: prefill {pre_ms.mean()*1e3:.1f} us "
+              f"({flops / (pre_ms.mean() * 1e-3) / 1e12:.1f} TFLOP/s)", flush=True)
+        del x
+    return res
+
+
+# ---- CPU baseline: the oracle, unchanged, on a bounded sample -------------
+def cpu_baseline(seconds):
+    from oracle import attention as o_attn
+    from oracle import paged as o_paged
+    from workloads import make_workload, sentinel_pool
+
+    w = make_workload(3)
+    order = np.random.default_rng(0).permutation(w.batch)
+    kp = sentinel_pool(w.num_pages, w.num_kv_heads, w.page_size, w.head_dim, w.dtype)
+    vp = sentinel_pool(w.num_pages, w.num_kv_heads, w.page_size, w.head_dim, w.dtype)
+    done, nbytes, busy = [], 0, 0.0
+    ru0 = resource.getrusage(resource.RUSAGE_SELF)
+    for r in order.tolist():
+        d = w.request(r)
+        t0 = time.perf_counter()
+        o_paged.kv_write(kp, vp, d.k_cached, d.v_cached, w.cached_slots(r), w.page_size)
+        o_paged.kv_write(kp, vp, d.k_new, d.v_new, w.new_slots(r), w.page_size)
+        o_attn.paged_decode(d.q, kp, vp, w.block_tables[r:r + 1], w.context_lens[r:r + 1],
+                            w.scale, w.page_size, w.dtype)
+        busy += time.perf_counter() - t0
+        done.append(r)
+        nbytes += int(w.context_lens[r]) * w.num_kv_heads * w.head_dim * 2 * 2
+        if busy >= seconds:
+            break
+    ru1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu = (ru1.ru_utime - ru0.ru_utime) + (ru1.ru_stime - ru0.ru_stime)
+    cores = max(1, int(round(cpu / max(busy, 1e-9))))
+    return dict(value=nbytes / busy / 1e9, unit="GB/s", cores=cores, kind="oracle",
+                sample=f"scatter write + fp64 decode of {len(done)} of the 256 decode-b256 "
+                       f"requests ({nbytes / 1e6:.0f} MB of K/V), {busy:.1f} s; "
+                       f"host has {len(os.sched_getaffinity(0))} usable cores")
+
+
+def traffic_for(kernel_file, launches_bytes_key):
+    """HBM bytes per launch from committed counter runs, only while the
+    kernel source is unchanged since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        table = json.load(f)
+    entry = table.get(launches_bytes_key)
+    if not entry:
+        return None
+    src = os.path.join(ROOT, "paged_kv_attention_16_amd", "csrc", kernel_file)
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if entry.get("source_sha256") != sha:
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no "
+              f"multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    res = gpu_legs(args)
+    dec = res["decode"]
+    w = dec["workload"]
+    value = dec["step_bytes"] / (dec["step_ms"] * 1e-3) / 1e9
+    achieved = dec["dec_bytes"] / (dec["dec_ms"] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode-b256: 256 requests, Hq 16 / Hkv 8, head_dim 128, page 256, "
+                        "context U[16,1024]+U[0,1024], step = write 256 new tokens + paged decode",
+            "batch": int(w.batch),
+            "total_context_tokens": int(w.context_lens.sum()),
+            "max_context": int(w.context_lens.max()),
+            "page_size": int(w.page_size),
+            "mall_flush": not args.no_flush,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "qil_paged_decode (decode_split_kernel + decode_merge_kernel)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_for("decode.hip", "decode-b256"),
+            "algorithmic_bytes_per_launch": int(dec["dec_bytes"]),
+            "launch_us_mean": round(dec["dec_ms"] * 1e3, 2),
+            "launch_us_median": round(dec["dec_ms_median"] * 1e3, 2),
+            "launch_us_p10": round(dec["dec_ms_p10"] * 1e3, 2),
+            "launch_us_p90": round(dec["dec_ms_p90"] * 1e3, 2),
+        },
+        "decode_tokens_per_s": round(w.batch / (dec["step_ms"] * 1e-3), 1),
+    }
+    if "prefill" in res:
+        p = res["prefill"]
+        tf = p["flops"] / (p["pre_ms"] * 1e-3) / 1e12
+        line["prefill"] = {
+            "workload": "prefill-varlen: 8 requests, cached prefix U[0,512] + chunk U[32,2048], "
+                        "Hq 16 / Hkv 8, page 16",
+            "bound": "mfma",
+            "achieved": round(tf, 2),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            "causal_flops": int(p["flops"]),
+            "launch_us_mean": round(p["pre_ms"] * 1e3, 2),
+            "launch_us_median": round(p["pre_ms_median"] * 1e3, 2),
+            "step_us_mean": round(p["step_ms"] * 1e3, 2),
+            "traffic": traffic_for("prefill.hip", "prefill-varlen"),
+        }
+    if not args.skip_cpu:
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

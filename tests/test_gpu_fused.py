@@ -1,0 +1,116 @@
+"""The fused Q/K RMSNorm + RoPE + scatter write and the mixed step of the
+Qwen3-8B-shaped workload (32 query heads / 8 KV heads, 64 decode requests
+and 4 prefill chunks of 512 per layer), against the oracle.
+
+The fused rows are rounded to bf16 at the same three points on both sides,
+but the GPU works in fp32 and the oracle in fp64, so a rounding tie can
+fall differently: rotated rows may differ by at most 2 bf16 ulps and only in
+a small fraction of elements; v and the placement are bit-exact."""
+
+import numpy as np
+import pytest
+import torch
+
+from tests import harness as H
+from oracle import norm_rope as o_nr
+from workloads import make_workload, sentinel_pool
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def ulp_diff(a_bits, b_bits):
+    """|a - b| in bf16 ulps for same-sign finite values (ordered integers)."""
+    def ordered(x):
+        x = x.astype(np.int32)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+def test_rope_table_matches_oracle(qil):
+    table = torch.empty(8192, 128, dtype=torch.float32, device=DEV)
+    qil.rope_cos_sin(table, 1.0e6)
+    torch.cuda.synchronize()
+    mine = table.cpu().numpy()
+    ref = o_nr.rope_table(8192, 128, 1.0e6)
+    d = np.abs(mine.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    print("rope table: entries differing", int((d > 0).sum()), "max ulp", int(d.max()), flush=True)
+    assert d.max() <= 1 and (d > 0).mean() < 1e-4
+
+
+def fused_case(qil, w, table_dev, data):
+    dev = DEV
+    kp, vp = H.device_pools(w, dev)
+    qil.kv_write(H.to_dev(data["k_cached"], "bf16", dev), H.to_dev(data["v_cached"], "bf16", dev),
+                 kp, vp, H.i32(data["cached_slots"], dev))
+    qw, kw = w.norm_weights()
+    q = H.to_dev(data["q"], "bf16", dev)
+    q_out = torch.empty_like(q)
+    fuse = qil.QKNormRope(q, q_out, H.to_dev(qw, "bf16", dev), H.to_dev(kw, "bf16", dev),
+                          H.i32(w.positions_new(), dev), table_dev, eps=w.eps)
+    qil.kv_write(H.to_dev(data["k_new"], "bf16", dev), H.to_dev(data["v_new"], "bf16", dev),
+                 kp, vp, H.i32(data["new_slots"], dev), fuse=fuse)
+    return data, kp, vp, q_out
+
+
+def test_fused_write_stage(qil):
+    w = make_workload(5)
+    print("cfg5 layer 0: tokens", int(w.new_lens.sum()), flush=True)
+    data = w.gather()
+    k_ref, q_ref, table = H.oracle_fused(w, data)
+    table_dev = torch.from_numpy(table).to(DEV)        # same table on both sides
+    data, kp, vp, q_out = fused_case(qil, w, table_dev, data)
+    torch.cuda.synchronize()
+    qd = ulp_diff(H.to_bits(q_out), q_ref)
+    kb = H.to_bits(kp).reshape(w.num_pages, 8, 16, 128)
+    vb = H.to_bits(vp).reshape(w.num_pages, 8, 16, 128)
+    slots = data["new_slots"]
+    pg, off = slots // 16, slots % 16
+    kd = ulp_diff(kb[pg, :, off], k_ref)
+    assert np.array_equal(vb[pg, :, off], data["v_new"])
+    print(f"fused: q non-exact {np.mean(qd > 0):.2e} max {qd.max()} ulp; "
+          f"k non-exact {np.mean(kd > 0):.2e} max {kd.max()} ulp", flush=True)
+    assert qd.max() <= 2 and kd.max() <= 2
+    assert np.mean(qd > 0) < 1e-3 and np.mean(kd > 0) < 1e-3
+    # every slot not written this step still holds what it held before
+    mask = np.ones((w.num_pages, 16), bool)
+    mask[pg, off] = False
+    cached = data["cached_slots"]
+    mask[cached // 16, cached % 16] = False
+    assert np.all(kb.transpose(0, 2, 1, 3)[mask] == 0x7FC0)
+
+
+@pytest.mark.parametrize("layer", [0, 35])
+def test_mixed_step_chain(qil, layer):
+    """Fused write -> decode (64 requests) -> prefill (4 chunks) with the
+    library's own RoPE table, against the oracle's own chain."""
+    w = make_workload(5, layer)
+    table_dev = torch.empty(w.max_position, 128, dtype=torch.float32, device=DEV)
+    qil.rope_cos_sin(table_dev, w.theta)
+    data, kp, vp, q_out = fused_case(qil, w, table_dev, w.gather())
+    dec_rows = torch.from_numpy(np.arange(64)).to(DEV)
+    q_dec = q_out.index_select(0, dec_rows).contiguous()
+    bt = H.i32(w.block_tables, DEV)
+    ctx = H.i32(w.context_lens, DEV)
+    out_dec = torch.empty_like(q_dec)
+    qil.paged_decode(out_dec, q_dec, kp, vp, bt[:64].contiguous(), ctx[:64].contiguous(),
+                     int(w.context_lens[:64].max()), float(w.scale))
+    q_pre = q_out[64:].contiguous()
+    out_pre = torch.empty_like(q_pre)
+    pre = w.prefill_idx
+    qil.paged_prefill(out_pre, q_pre, kp, vp, bt[64:].contiguous(), H.i32(w.cu_seqlens(pre), DEV),
+                      ctx[64:].contiguous(), 512, int(w.context_lens[64:].max()), float(w.scale))
+    torch.cuda.synchronize()
+
+    k_ref, q_ref, _ = H.oracle_fused(w, data)
+    oc = H.OracleCase(w, data, list(range(0, 64, 9)) + [64, 67], k_new=k_ref, q=q_ref)
+    dsel = list(range(0, 64, 9))
+    ref_dec = oc.attention(dsel)
+    got_dec = H.to_f64(out_dec)[dsel]
+    ref_pre = oc.attention([64, 67])
+    got_pre = H.to_f64(out_pre)
+    got_pre = np.concatenate([got_pre[0:512], got_pre[3 * 512:4 * 512]])
+    print(f"layer {layer}: decode max err {np.max(np.abs(got_dec - ref_dec)):.3e}, "
+          f"prefill max err {np.max(np.abs(got_pre - ref_pre)):.3e}", flush=True)
+    assert H.excess(got_dec, ref_dec, "bf16") <= 0
+    assert H.excess(got_pre, ref_pre, "bf16") <= 0

@@ -1,0 +1,89 @@
+"""qil_paged_prefill on the GPU against the oracle: the varlen workload in
+full, ragged and degenerate chunks, every GQA group size, several page
+sizes, decode == prefill with one query token, and chunking invariance."""
+
+import numpy as np
+import pytest
+import torch
+
+from tests import harness as H
+from workloads import make_workload, make_custom
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def test_cfg4_full(qil):
+    w = make_workload(4)
+    print("cfg4 chunks", w.new_lens.tolist(), "prefix", w.cached_lens.tolist(), flush=True)
+    case = H.DeviceCase(w, DEV)
+    out = H.to_f64(case.prefill())
+    ref = H.OracleCase(w, case.data, range(w.batch)).attention(range(w.batch))
+    print("cfg4 max abs err", np.max(np.abs(out - ref)), flush=True)
+    assert H.excess(out, ref, "bf16") <= 0
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (32, 8), (16, 2)])
+def test_group_sizes_ragged(qil, hq, hkv):
+    # chunk lengths straddle the query tile (128 / G tokens) and key tile (64)
+    ctx = [1, 65, 200, 129, 700, 33]
+    new = [1, 1, 200, 64, 131, 17]
+    got, ref = H.run_small_prefill(DEV, ctx, new, hq, hkv, 16, seed=hq * 10 + hkv)
+    assert H.excess(got, ref, "bf16") <= 0
+
+
+@pytest.mark.parametrize("page", [32, 64, 256])
+def test_page_sizes(qil, page):
+    got, ref = H.run_small_prefill(DEV, [300, 1000, 90], [100, 257, 90], 16, 8, page, seed=page)
+    assert H.excess(got, ref, "bf16") <= 0
+
+
+def test_decode_equals_prefill_one_token(qil):
+    w = make_custom([1, 17, 300, 1024, 77], [1] * 5, page=16, seed=21, decode=True)
+    case = H.DeviceCase(w, DEV)
+    dec = H.to_f64(case.decode())
+    pre = H.to_f64(case.prefill(requests=np.arange(5)))
+    assert np.max(np.abs(dec - pre)) < 1e-2
+
+
+def test_chunking_invariance(qil):
+    # the whole prompt as one chunk vs three irregular chunks over the same pool
+    L = 777
+    w = make_custom([L], [L], page=16, seed=22)
+    case = H.DeviceCase(w, DEV)
+    full = H.to_f64(case.prefill())
+    parts = []
+    for a, b in [(0, 100), (100, 101), (101, L)]:
+        q = case.q_all[a:b].contiguous()
+        out = torch.empty_like(q)
+        qil.paged_prefill(out, q, case.kp, case.vp, case.bt, H.i32([0, b - a], DEV),
+                          H.i32([b], DEV), b - a, b, float(w.scale))
+        parts.append(H.to_f64(out))
+    assert np.max(np.abs(np.concatenate(parts) - full)) < 1e-2
+    ref = H.OracleCase(w, case.data, [0]).attention([0])
+    assert H.excess(full, ref, "bf16") <= 0
+
+
+def test_zero_length_request_is_skipped(qil):
+    w = make_custom([50, 20, 64], [10, 1, 64], page=16, seed=23)
+    case = H.DeviceCase(w, DEV)
+    # request 1 gets no new tokens in this call
+    reqs = np.array([0, 1, 2])
+    rows = torch.from_numpy(np.concatenate([case.rows_of([0]), case.rows_of([2])])).to(DEV)
+    q = case.q_all.index_select(0, rows).contiguous()
+    cu = H.i32([0, 10, 10, 74], DEV)
+    ctx = H.i32([50, 19, 64], DEV)
+    out = torch.empty_like(q)
+    qil.paged_prefill(out, q, case.kp, case.vp, case.bt, cu, ctx, 64, 64, float(w.scale))
+    got = H.to_f64(out)
+    ref = H.OracleCase(w, case.data, [0, 2]).attention([0, 2])
+    assert H.excess(got, ref, "bf16") <= 0
+    del reqs
+
+
+def test_run_twice_bitwise(qil):
+    w = make_workload(4)
+    case = H.DeviceCase(w, DEV)
+    a = H.to_bits(case.prefill())
+    b = H.to_bits(case.prefill())
+    assert np.array_equal(a, b)

@@ -9,6 +9,6 @@ consume what it returns.
 """
 
 from .configs import (  # noqa: F401
-    Workload, RequestData, make_workload, config_names, CONFIGS,
+    Workload, RequestData, make_workload, make_custom, config_names, CONFIGS,
     bf16_from_f32, sentinel_pool,
 )

@@ -301,3 +301,29 @@ def make_workload(cfg, layer=0):
         fused=(cfg == 5), eps=spec.get("eps", 1e-6), theta=spec.get("theta", 1e6),
         max_position=spec.get("max_position", 0),
     )
+
+
+def make_custom(context, new, hq=16, hkv=8, page=16, dtype="bf16", seed=0, spare_pages=7,
+                decode=False):
+    """A small ad-hoc workload with the same structure as the five configs
+    (edge cases of the tests): given context lengths and new-token counts
+    per request, pages placed by a seeded permutation with spare pages."""
+    context = np.asarray(context, dtype=np.int64)
+    new = np.asarray(new, dtype=np.int64)
+    rng = _rng(1000 + seed, 0, 0)
+    need = -(-context // page)
+    num_pages = int(need.sum()) + spare_pages
+    perm = rng.permutation(num_pages).astype(np.int32)
+    stride = max(1, int(need.max()))
+    tables = np.full((len(context), stride), -1, dtype=np.int32)
+    at = 0
+    for r, k in enumerate(need.tolist()):
+        tables[r, :k] = perm[at:at + k]
+        at += k
+    idx = np.arange(len(context))
+    empty = np.arange(0)
+    return Workload(
+        cfg=1000 + seed, layer=0, name=f"custom-{seed}", dtype=dtype, num_q_heads=hq,
+        num_kv_heads=hkv, head_dim=HEAD_DIM, page_size=page, num_pages=num_pages,
+        cached_lens=context - new, new_lens=new, block_tables=tables,
+        decode_idx=idx if decode else empty, prefill_idx=empty if decode else idx)
