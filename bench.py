@@ -50,7 +50,34 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="time torch's copy and sum over 1 GiB (reference ceilings and the "
+                         "plain copy kernel used to scale HBM byte counters), then exit")
     return ap.parse_args()
+
+
+def calibrate(steps):
+    """Plain library kernels of known size: a 1 GiB device-to-device copy
+    (reads 1 GiB, writes 1 GiB) and a 1 GiB bf16 sum (reads 1 GiB)."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = (1 << 30) // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    out = {}
+    for name, fn, nbytes in (("copy_1GiB", lambda: dst.copy_(src), 2 << 30),
+                             ("sum_1GiB", lambda: src.sum(dtype=torch.float32), 1 << 30)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            a.record(); fn(); b.record()
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        out[name] = dict(us=round(ms * 1e3, 1), gbs=round(nbytes / (ms * 1e-3) / 1e9, 1))
+    print(json.dumps({"calibration": out}), flush=True)
 
 
 # ---- device inputs (workload bits -> tensors, written through the library) ---
@@ -255,6 +282,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no "
               f"multi-GPU path.", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate:
+        calibrate(args.steps)
+        return
     res = gpu_legs(args)
     dec = res["decode"]
     w = dec["workload"]

@@ -30,10 +30,12 @@
  *    num_q_heads must be num_kv_heads * G with G in {1, 2, 4, 8}.
  *  - dtype: QIL_F32 (IEEE binary32) or QIL_BF16 (bfloat16).  Outputs have the
  *    input dtype; accumulation is fp32.  Pointers must be 16-byte aligned.
- *  - Device-resident metadata (slots, page ids, lengths) is a precondition.
- *    The kernels never dereference an out-of-range page id or slot: such
- *    entries are treated as absent (a write is skipped; a key row reads as
- *    zero).  They are not reported.
+ *  - Device-resident metadata (slots, page ids, lengths) is a precondition,
+ *    not checked.  The kernels still never dereference an out-of-range page
+ *    id or slot and never read a block-table row past max_context_len: a
+ *    write to such a slot is skipped, and the attention output of a request
+ *    whose table holds such a page is unspecified (but finite memory is all
+ *    that is touched).
  *
  * KV pool layout (the "paged KV cache")
  * -------------------------------------
@@ -155,7 +157,7 @@ int qil_rope_cos_sin(float* cos_sin, int32_t max_position, int32_t head_dim, dou
  *   context_lens   int32 [batch], each in [1, block_table_stride*page_size]
  *   max_context_len host int >= every context_lens[r] (sizes the split grid)
  *   scale          multiplies q.k before the softmax (fp32)
- *   keys_per_split 0 = automatic, else a multiple of 64: the context of each
+ *   keys_per_split 0 = automatic, else a multiple of 64 up to 4096: the context of each
  *                  request is cut into splits of this many keys, each split
  *                  reduced by its own workgroup, then merged by a second
  *                  kernel through the log-sum-exp rule.

@@ -74,26 +74,25 @@ struct SplitPlan {
   int32_t num_splits;
 };
 
-constexpr int32_t kMaxSplits = 1024;
+constexpr int32_t kMaxSplits = 65535;
+constexpr int32_t kMaxKeysPerSplit = 4096;  // 64 steps of 64 keys: one page id per lane
 
 SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t max_context_len,
                       int32_t keys_per_split) {
   SplitPlan p;
   int32_t S = keys_per_split;
   if (S <= 0) {
-    // Aim at ~4096 non-empty workgroups assuming contexts average half the
-    // maximum, never below 128 keys per split.
+    // Long contiguous streams per workgroup read HBM fastest, so split only
+    // as far as needed for ~1024 non-empty workgroups (contexts assumed to
+    // average half the maximum), with 256 .. 4096 keys per split.
     const int64_t pairs = (int64_t)batch * num_kv_heads;
-    int64_t s = (pairs * (int64_t)max_context_len) / (2 * 4096);
+    int64_t s = (pairs * (int64_t)max_context_len) / (2 * 1024);
     s = (s + 63) / 64 * 64;
-    if (s < 128) s = 128;
-    S = (int32_t)(s > (1 << 30) ? (1 << 30) : s);
+    if (s < 256) s = 256;
+    if (s > kMaxKeysPerSplit) s = kMaxKeysPerSplit;
+    S = (int32_t)s;
   }
-  int64_t n = ((int64_t)max_context_len + S - 1) / S;
-  if (n > kMaxSplits) {
-    S = (int32_t)(((((int64_t)max_context_len + kMaxSplits - 1) / kMaxSplits) + 63) / 64 * 64);
-    n = ((int64_t)max_context_len + S - 1) / S;
-  }
+  const int64_t n = ((int64_t)max_context_len + S - 1) / S;
   p.keys_per_split = S;
   p.num_splits = (int32_t)(n < 1 ? 1 : n);
   return p;
@@ -187,8 +186,9 @@ size_t qil_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32
                                        int32_t keys_per_split) {
   (void)page_size;
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len <= 0) return 0;
-  if (keys_per_split < 0 || keys_per_split % 64) return 0;
+  if (keys_per_split < 0 || keys_per_split % 64 || keys_per_split > kMaxKeysPerSplit) return 0;
   const SplitPlan p = plan_splits(batch, num_kv_heads, max_context_len, keys_per_split);
+  if (p.num_splits > kMaxSplits) return 0;
   return workspace_bytes_for(batch, num_q_heads, p);
 }
 
@@ -202,9 +202,9 @@ int qil_paged_decode(void* out, const void* q, const void* k_cache, const void* 
   if (dtype != QIL_F32 && dtype != QIL_BF16) return fail(QIL_EUNSUPPORTED, "dtype %d", dtype);
   int rc = check_common(num_q_heads, num_kv_heads, head_dim, page_size, num_pages);
   if (rc) return rc;
-  if (keys_per_split < 0 || keys_per_split % 64)
-    return fail(QIL_EINVAL, "keys_per_split %d must be 0 or a positive multiple of 64",
-                keys_per_split);
+  if (keys_per_split < 0 || keys_per_split % 64 || keys_per_split > kMaxKeysPerSplit)
+    return fail(QIL_EINVAL, "keys_per_split %d must be 0 or a multiple of 64 up to %d",
+                keys_per_split, kMaxKeysPerSplit);
   if (batch == 0) return ok();
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(QIL_EINVAL, "null pointer argument");
@@ -216,6 +216,9 @@ int qil_paged_decode(void* out, const void* q, const void* k_cache, const void* 
     return fail(QIL_EINVAL, "max_context_len %d exceeds block_table_stride*page_size", max_context_len);
   if (!(scale == scale)) return fail(QIL_EINVAL, "scale is NaN");
   const SplitPlan p = plan_splits(batch, num_kv_heads, max_context_len, keys_per_split);
+  if (p.num_splits > kMaxSplits)
+    return fail(QIL_EINVAL, "max_context_len %d needs %d splits (at most %d)", max_context_len,
+                p.num_splits, kMaxSplits);
   const size_t need = workspace_bytes_for(batch, num_q_heads, p);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return fail(QIL_EWORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need,

@@ -23,6 +23,8 @@
 //
 // Kernel 2 (merge): one workgroup per (query head, request) combines the
 // splits: m* = max m_s, l = sum 2^(m_s - m*) l_s, o = sum 2^(m_s - m*) o_s / l.
+#include <type_traits>
+
 #include "device_common.h"
 #include "qil_internal.h"
 
@@ -48,15 +50,28 @@ struct RowChunk {
   uint4 a, b;  // b unused for bf16
 };
 
-template <bool BF16>
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load; K/V rows are streamed once per call, so they are loaded
+// non-temporally (they should not displace reusable lines from the caches).
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const char* p) {
+  if (NT) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  }
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+template <bool BF16, bool NT = false>
 __device__ __forceinline__ RowChunk<BF16> load_chunk(const char* row, int j) {
   RowChunk<BF16> c;
   if (BF16) {
-    c.a = *reinterpret_cast<const uint4*>(row + 16 * j);
+    c.a = load16<NT>(row + 16 * j);
     c.b = make_uint4(0, 0, 0, 0);
   } else {
-    c.a = *reinterpret_cast<const uint4*>(row + 16 * j);
-    c.b = *reinterpret_cast<const uint4*>(row + 256 + 16 * j);
+    c.a = load16<NT>(row + 16 * j);
+    c.b = load16<NT>(row + 256 + 16 * j);
   }
   return c;
 }
@@ -78,13 +93,41 @@ __device__ __forceinline__ void unpack(const RowChunk<BF16>& c, float x[8]) {
   }
 }
 
-// Sum over the 16 lanes of a row (xor butterfly inside each 16-lane group).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
+// Sum over the 16 lanes of a row with DPP: swap neighbours, swap pairs,
+// mirror within 8, mirror within 16.  Every lane ends with the same sum.
 __device__ __forceinline__ float row_sum16(float x) {
-  x += __shfl_xor(x, 1, 16);
-  x += __shfl_xor(x, 2, 16);
-  x += __shfl_xor(x, 4, 16);
-  x += __shfl_xor(x, 8, 16);
+  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_mov<0x141>(x);  // row_half_mirror
+  x += dpp_mov<0x140>(x);  // row_mirror
   return x;
+}
+
+// Partial dot product of this lane's 8 elements of q and k.
+template <bool BF16>
+__device__ __forceinline__ float dot8(const uint32_t qraw[4], const float qf[8],
+                                      const RowChunk<BF16>& k) {
+  if (BF16) {
+    const uint32_t kw[4] = {k.a.x, k.a.y, k.a.z, k.a.w};
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qraw[i]),
+                                            __builtin_bit_cast(bf16x2_t, kw[i]), acc, false);
+    return acc;
+  } else {
+    float kx[8];
+    unpack<BF16>(k, kx);
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(qf[e], kx[e], acc);
+    return acc;
+  }
 }
 
 template <int G, bool BF16>
@@ -106,20 +149,24 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int eb = BF16 ? 2 : 4;
   const int64_t row_bytes = (int64_t)kHeadDim * eb;
 
-  // q of the G heads of this KV head, pre-scaled into the base-2 domain.
+  // q of the G heads of this KV head.  bf16: raw pairs for v_dot2 and the
+  // scale (into the base-2 domain) applied to the score; fp32: pre-scaled.
   const float qs = a.scale * kLog2e;
-  float qv[G][8];
+  uint32_t qraw[G][4];
+  float qf[G][8];
   {
     const char* qbase = static_cast<const char*>(a.q) +
                         ((int64_t)r * a.num_q_heads + (int64_t)g * G) * row_bytes;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       RowChunk<BF16> c = load_chunk<BF16>(qbase + h * row_bytes, j);
-      unpack<BF16>(c, qv[h]);
+      qraw[h][0] = c.a.x; qraw[h][1] = c.a.y; qraw[h][2] = c.a.z; qraw[h][3] = c.a.w;
+      unpack<BF16>(c, qf[h]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qv[h][e] *= qs;
+      for (int e = 0; e < 8; ++e) qf[h][e] *= qs;
     }
   }
+  const float score_scale = BF16 ? qs : 1.0f;
 
   float m[G], l[G], o[G][8];
 #pragma unroll
@@ -134,62 +181,65 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const char* kbase = static_cast<const char*>(a.k_cache);
   const char* vbase = static_cast<const char*>(a.v_cache);
 
-  for (int kb = kbeg; kb < kend; kb += kKeysPerStep) {
-    const int key0 = kb + 16 * w;  // first key of this wavefront (wave-uniform)
-    if (key0 >= kend) continue;    // uniform per wavefront
-    const int page = bt_row[key0 >> a.log2_page];
-    const bool page_ok = (unsigned)page < (unsigned)a.num_pages;
-    const int64_t row0 = ((int64_t)page * a.num_kv_heads + g) * P + (key0 & (P - 1));
+  // Group i of this wavefront covers keys kbeg + 64 i + 16 w .. +15, inside
+  // one page.  Lane i holds the page id of group i (a split has at most 64
+  // groups per wavefront), read into a scalar register when the group's loads
+  // are issued, so no load waits on the block table inside the loop.
+  const int first = kbeg + 16 * w;
+  const int ngroups = first < kend ? (kend - first + kKeysPerStep - 1) / kKeysPerStep : 0;
+  const int nfull = first + 16 <= kend ? (kend - first - 16) / kKeysPerStep + 1 : 0;
+  int page_of_lane = -1;
+  if (lane < ngroups) page_of_lane = bt_row[(first + kKeysPerStep * lane) >> a.log2_page];
 
-    RowChunk<BF16> kc[4], vc[4];
-    bool valid[4];
+  struct Group {
+    RowChunk<BF16> k[4], v[4];
+    bool ok;
+  };
+
+  auto load_group = [&](auto full_tag, int i, Group& gr) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    const int key0 = first + kKeysPerStep * i;
+    const int page = __builtin_amdgcn_readlane(page_of_lane, i);
+    gr.ok = (unsigned)page < (unsigned)a.num_pages;
+    const int64_t row0 = ((int64_t)page * a.num_kv_heads + g) * P + (key0 & (P - 1));
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int key = key0 + 4 * u + row;
-      valid[u] = page_ok && key < kend;
-      if (valid[u]) {
-        const int64_t off = (row0 + 4 * u + row) * row_bytes;
-        kc[u] = load_chunk<BF16>(kbase + off, j);
-        vc[u] = load_chunk<BF16>(vbase + off, j);
+      const int64_t off = (row0 + 4 * u + row) * row_bytes;
+      const bool valid = gr.ok && (FULL || key0 + 4 * u + row < kend);
+      if (FULL ? gr.ok : valid) {
+        gr.k[u] = load_chunk<BF16, true>(kbase + off, j);
+        gr.v[u] = load_chunk<BF16, true>(vbase + off, j);
       } else {
-        kc[u].a = kc[u].b = vc[u].a = vc[u].b = make_uint4(0, 0, 0, 0);
+        gr.k[u].a = gr.k[u].b = gr.v[u].a = gr.v[u].b = make_uint4(0, 0, 0, 0);
       }
     }
+  };
 
+  auto compute_group = [&](auto full_tag, int i, const Group& gr) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    const int key0 = first + kKeysPerStep * i;
     float s[4][G];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      float kx[8];
-      unpack<BF16>(kc[u], kx);
+      const bool valid = gr.ok && (FULL || key0 + 4 * u + row < kend);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf(qv[h][e], kx[e], acc);
-        acc = row_sum16(acc);
-        s[u][h] = valid[u] ? acc : -INFINITY;
+        const float acc = row_sum16(dot8<BF16>(qraw[h], qf[h], gr.k[u])) * score_scale;
+        s[u][h] = valid ? acc : -INFINITY;
       }
     }
-
     float vx[4][8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) unpack<BF16>(vc[u], vx[u]);
-
+    for (int u = 0; u < 4; ++u) unpack<BF16>(gr.v[u], vx[u]);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float mt = m[h];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) mt = fmaxf(mt, s[u][h]);
+      const float mt = fmaxf(fmaxf(m[h], fmaxf(s[0][h], s[1][h])), fmaxf(s[2][h], s[3][h]));
       const float corr = fast_exp2(m[h] - mt);
       m[h] = mt;
       float p[4];
-      float psum = 0.f;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        p[u] = fast_exp2(s[u][h] - mt);
-        psum += p[u];
-      }
-      l[h] = l[h] * corr + psum;
+      for (int u = 0; u < 4; ++u) p[u] = fast_exp2(s[u][h] - mt);
+      l[h] = fmaf(l[h], corr, (p[0] + p[1]) + (p[2] + p[3]));
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float acc = o[h][e] * corr;
@@ -198,6 +248,23 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         o[h][e] = acc;
       }
     }
+  };
+
+  // Full groups, two in flight: the next group's loads are issued before the
+  // current group is computed.
+  Group ga, gb;
+  if (nfull > 0) load_group(std::true_type{}, 0, ga);
+  for (int i = 0; i < nfull; i += 2) {
+    if (i + 1 < nfull) load_group(std::true_type{}, i + 1, gb);
+    compute_group(std::true_type{}, i, ga);
+    if (i + 1 < nfull) {
+      if (i + 2 < nfull) load_group(std::true_type{}, i + 2, ga);
+      compute_group(std::true_type{}, i + 1, gb);
+    }
+  }
+  if (ngroups > nfull) {  // the context ends inside this wavefront's last group
+    load_group(std::false_type{}, nfull, ga);
+    compute_group(std::false_type{}, nfull, ga);
   }
 
   // Merge the 4 rows of this wavefront (lanes 16 and 32 apart).

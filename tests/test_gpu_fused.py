@@ -3,9 +3,13 @@ Qwen3-8B-shaped workload (32 query heads / 8 KV heads, 64 decode requests
 and 4 prefill chunks of 512 per layer), against the oracle.
 
 The fused rows are rounded to bf16 at the same three points on both sides,
-but the GPU works in fp32 and the oracle in fp64, so a rounding tie can
-fall differently: rotated rows may differ by at most 2 bf16 ulps and only in
-a small fraction of elements; v and the placement are bit-exact."""
+but the GPU works in fp32 and the oracle in fp64, so a value that lands
+within fp32 error of a bf16 tie can round the other way.  Before the
+rotation that moves y by one bf16 ulp (at most 2^-7 relative), and the
+rotation carries it into the output as at most 2^-6 (|y_a cos| + |y_b sin|)
+-- far more than one output ulp where the two products cancel.  The bar:
+every element within one output ulp plus that bound, and fewer than 1e-3 of
+the elements not bit-exact.  v and the placement are bit-exact."""
 
 import numpy as np
 import pytest
@@ -13,18 +17,32 @@ import torch
 
 from tests import harness as H
 from oracle import norm_rope as o_nr
+from oracle.bf16 import bf16_to_f64, round_bf16
 from workloads import make_workload, sentinel_pool
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-def ulp_diff(a_bits, b_bits):
-    """|a - b| in bf16 ulps for same-sign finite values (ordered integers)."""
-    def ordered(x):
-        x = x.astype(np.int32)
-        return np.where(x & 0x8000, -(x & 0x7FFF), x)
-    return np.abs(ordered(a_bits) - ordered(b_bits))
+def rotation_bound(x_bits, w_bits, eps, cos, sin):
+    """2^-6 (|y_a cos| + |y_b sin|) per output element, from the oracle's
+    own rounded y (the row after RMSNorm and the weight product)."""
+    y = round_bf16(round_bf16(o_nr.rms_normalize(bf16_to_f64(x_bits), eps)) * bf16_to_f64(w_bits))
+    half = y.shape[-1] // 2
+    y1, y2 = np.abs(y[..., :half]), np.abs(y[..., half:])
+    c, s = np.abs(cos), np.abs(sin)
+    return 2.0 ** -6 * np.concatenate([y1 * c + y2 * s, y2 * c + y1 * s], axis=-1)
+
+
+def check_rotated(got_bits, ref_bits, x_bits, w_bits, eps, cos, sin, what):
+    got, ref = bf16_to_f64(got_bits), bf16_to_f64(ref_bits)
+    ulp = np.maximum(np.abs(ref), 2.0 ** -126) * 2.0 ** -7
+    bound = ulp + rotation_bound(x_bits, w_bits, eps, cos, sin)
+    inexact = np.mean(got_bits != ref_bits)
+    worst = np.max(np.abs(got - ref) / bound)
+    print(f"fused {what}: non-exact fraction {inexact:.2e}, worst |diff|/bound {worst:.3f}", flush=True)
+    assert inexact < 1e-3
+    assert np.all(np.abs(got - ref) <= bound)
 
 
 def test_rope_table_matches_oracle(qil):
@@ -61,17 +79,17 @@ def test_fused_write_stage(qil):
     table_dev = torch.from_numpy(table).to(DEV)        # same table on both sides
     data, kp, vp, q_out = fused_case(qil, w, table_dev, data)
     torch.cuda.synchronize()
-    qd = ulp_diff(H.to_bits(q_out), q_ref)
     kb = H.to_bits(kp).reshape(w.num_pages, 8, 16, 128)
     vb = H.to_bits(vp).reshape(w.num_pages, 8, 16, 128)
     slots = data["new_slots"]
     pg, off = slots // 16, slots % 16
-    kd = ulp_diff(kb[pg, :, off], k_ref)
     assert np.array_equal(vb[pg, :, off], data["v_new"])
-    print(f"fused: q non-exact {np.mean(qd > 0):.2e} max {qd.max()} ulp; "
-          f"k non-exact {np.mean(kd > 0):.2e} max {kd.max()} ulp", flush=True)
-    assert qd.max() <= 2 and kd.max() <= 2
-    assert np.mean(qd > 0) < 1e-3 and np.mean(kd > 0) < 1e-3
+    qw, kw = w.norm_weights()
+    tab = table.astype(np.float64)
+    pos = w.positions_new()
+    cos, sin = tab[pos, :64][:, None, :], tab[pos, 64:][:, None, :]
+    check_rotated(H.to_bits(q_out), q_ref, data["q"], qw, w.eps, cos, sin, "q")
+    check_rotated(kb[pg, :, off], k_ref, data["k_new"], kw, w.eps, cos, sin, "k")
     # every slot not written this step still holds what it held before
     mask = np.ones((w.num_pages, 16), bool)
     mask[pg, off] = False
