@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     bool ok;
   };
 
-  auto load_group = [&](auto full_tag, int i, Group& gr) {
+  auto load_group = [&](auto full_tag, int i, Group& gr) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(full_tag)::value;
     const int key0 = first + kKeysPerStep * i;
     const int page = __builtin_amdgcn_readlane(page_of_lane, i);
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     }
   };
 
-  auto compute_group = [&](auto full_tag, int i, const Group& gr) {
+  auto compute_group = [&](auto full_tag, int i, const Group& gr) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(full_tag)::value;
     const int key0 = first + kKeysPerStep * i;
     float s[4][G];
