@@ -11,7 +11,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "../../include/qil.h"
+#include "qil.h"
 #include "qil_internal.h"
 
 namespace {

@@ -46,8 +46,6 @@ namespace qil {
 namespace {
 
 constexpr int kBN = 64;        // keys per tile
-constexpr int kRowsWG = 256;   // query rows per workgroup (8 wavefronts x 32)
-constexpr int kThreads = 512;
 constexpr float kLazyRescale = 8.0f;  // log2 of the largest weight allowed before rescaling
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -65,6 +63,22 @@ __device__ __forceinline__ int acc_row(int v, int hf) { return 8 * (v >> 2) + 4 
 // different 64-byte bank groups.
 __device__ __forceinline__ int k_chunk(int row, int c) { return c ^ (row & 15); }
 __device__ __forceinline__ int v_chunk(int row, int c) { return c ^ ((row & 3) << 2); }
+
+// Maximum / sum over the two halves of a wavefront (lanes l and l ^ 32),
+// with v_permlane32_swap instead of an LDS round trip.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+constexpr int kWaves = 8;               // wavefronts per workgroup, 32 query rows each
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsWG = 32 * kWaves;    // query rows per workgroup
+constexpr int kRowsPerWave = kBN / kWaves;  // tile rows each wavefront loads
 
 template <int G>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int n_qtiles) {
@@ -135,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int n_
   // Lane i holds the page id of this wavefront's rows in tile base + i.
   int page_lane = -1;
   auto fetch_pages = [&](int base) __attribute__((always_inline)) {
-    const int key = (base + lane) * kBN + 8 * w;
+    const int key = (base + lane) * kBN + kRowsPerWave * w;
     page_lane = key < L ? bt_row[key >> a.log2_page] : -1;
   };
 
@@ -143,12 +157,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int n_
     const int page = __builtin_amdgcn_readlane(page_lane, kt & 63);
     if ((unsigned)page >= (unsigned)a.num_pages) return;  // absent page (uniform)
 #pragma unroll
-    for (int m2 = 0; m2 < 2; ++m2) {
-      const int row = 8 * w + 4 * m2 + lrow;  // tile row this lane fills
+    for (int m2 = 0; m2 < kRowsPerWave / 4; ++m2) {
+      const int row = kRowsPerWave * w + 4 * m2 + lrow;  // tile row this lane fills
       const int key = kt * kBN + row;
       const int64_t grow = (((int64_t)page * a.num_kv_heads + g) << a.log2_page) + (key & (P - 1));
-      lds_char* kdst = (lds_char*)&smem[buf][0][0] + (8 * w + 4 * m2) * 256;
-      lds_char* vdst = (lds_char*)&smem[buf][1][0] + (8 * w + 4 * m2) * 256;
+      lds_char* kdst = (lds_char*)&smem[buf][0][0] + (kRowsPerWave * w + 4 * m2) * 256;
+      lds_char* vdst = (lds_char*)&smem[buf][1][0] + (kRowsPerWave * w + 4 * m2) * 256;
       if (key < L) {
         __builtin_amdgcn_global_load_lds(kpool + grow * 256 + 16 * k_chunk(row, lpc), kdst, 16, 0, 0);
         __builtin_amdgcn_global_load_lds(vpool + grow * 256 + 16 * v_chunk(row, lpc), vdst, 16, 0, 0);
@@ -187,15 +201,43 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int n_
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
   const f32x16_t zero16 = {};
 
-  auto qk_half = [&](int buf, int b) __attribute__((always_inline)) -> f32x16_t {
+  // Operand fetches are separate from the matrix instructions that use them,
+  // so a whole half-tile of LDS reads is in flight before its first MFMA.
+  auto load_k = [&](int buf, int b, bf16x8_t (&kop)[8]) __attribute__((always_inline)) {
     const char* krow = &smem[buf][0][0] + (32 * b + lq) * 256;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      kop[t] = *reinterpret_cast<const bf16x8_t*>(krow + 16 * ((2 * t + hf) ^ kx));
+  };
+  auto qk = [&](const bf16x8_t (&kop)[8]) __attribute__((always_inline)) -> f32x16_t {
     f32x16_t acc = zero16;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const bf16x8_t kop = *reinterpret_cast<const bf16x8_t*>(krow + 16 * ((2 * t + hf) ^ kx));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[t], acc, 0, 0, 0);
-    }
+    for (int t = 0; t < 8; ++t)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[t], qreg[t], acc, 0, 0, 0);
     return acc;
+  };
+  auto load_v = [&](int buf, int b, bf16x8_t (&vop)[4][2]) __attribute__((always_inline)) {
+    const lds_char* vbase = (const lds_char*)&smem[buf][1][0];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int s = 2 * b + s2;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(vbase + vofs[db] + (16 * s) * 256));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(vbase + vofs[db] + (16 * s + 8) * 256));
+        const i16x8_t v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        vop[db][s2] = __builtin_bit_cast(bf16x8_t, v8);
+      }
+    }
+  };
+  auto pv = [&](const bf16x8_t (&vop)[4][2], const bf16x8_t (&pb)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][s2], pb[s2], oacc[db], 0, 0, 0);
   };
 
   // Row maximum of a half and the lazy rescale (a uniform branch, rarely taken).
@@ -207,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int n_
       if (MASK && kbase + acc_row(v, hf) > my_pos) s[v] = -INFINITY;
       mx = fmaxf(mx, s[v]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * qs;
+    mx = max_halves(mx) * qs;
     if (__ballot(mx > mref + kLazyRescale) != 0) {
       const float mnew = fmaxf(mref, mx);
       const float corr = fast_exp2(mref - mnew);
@@ -238,37 +280,28 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int n_
     }
   };
 
-  auto pv_half = [&](int buf, int b, const bf16x8_t (&pb)[2]) __attribute__((always_inline)) {
-    const lds_char* vbase = (const lds_char*)&smem[buf][1][0];
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int s = 2 * b + s2;
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4_t*)(vbase + vofs[db] + (16 * s) * 256));
-        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4_t*)(vbase + vofs[db] + (16 * s + 8) * 256));
-        const i16x8_t v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, v8),
-                                                           pb[s2], oacc[db], 0, 0, 0);
-      }
-    }
-  };
-
-  // One tile: S^T of both halves, then the softmax of each half next to the
-  // matrix work of the other.
+  // One tile as two 32-key halves; each half's softmax sits next to the
+  // matrix work of the other half.
   auto compute = [&](auto mask_tag, int buf, int kt) __attribute__((always_inline)) {
     const int kbase = kt * kBN;
-    f32x16_t s0 = qk_half(buf, 0);
-    max_half(mask_tag, s0, kbase);
-    f32x16_t s1 = qk_half(buf, 1);
+    bf16x8_t kop[8];
+    bf16x8_t vop[4][2];
     bf16x8_t p0[2], p1[2];
+    load_k(buf, 0, kop);
+    f32x16_t s0 = qk(kop);
+    // all eight operand reads first, then the eight MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    load_k(buf, 1, kop);
+    max_half(mask_tag, s0, kbase);
+    f32x16_t s1 = qk(kop);
+    load_v(buf, 0, vop);
     exp_half(s0, p0);
     max_half(mask_tag, s1, kbase + 32);
-    pv_half(buf, 0, p0);
+    pv(vop, p0);
+    load_v(buf, 1, vop);
     exp_half(s1, p1);
-    pv_half(buf, 1, p1);
+    pv(vop, p1);
   };
 
   // Tiles [0, nfree) lie wholly at or before the first token's position and
@@ -294,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int n_
     for (int kt = nfree; kt < ntiles; ++kt) tile_step(std::true_type{}, kt);
   }
 
-  const float ltot = lrun + __shfl_xor(lrun, 32);
+  const float ltot = sum_halves(lrun);
   if (!row_valid) return;
   const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
   uint16_t* orow =
