@@ -227,17 +227,20 @@ def gpu_legs(args):
 
 # ---- CPU baseline: the oracle, unchanged, on a bounded sample -------------
 def cpu_baseline(seconds):
+    """The fp64 oracle on the host: the decode-b256 step (scatter write +
+    decode, every request; the whole workload fits in a few seconds) and, for
+    context, the prefill of as many prefill-varlen requests as fit in the
+    remaining time budget."""
     from oracle import attention as o_attn
     from oracle import paged as o_paged
     from workloads import make_workload, sentinel_pool
 
     w = make_workload(3)
-    order = np.random.default_rng(0).permutation(w.batch)
     kp = sentinel_pool(w.num_pages, w.num_kv_heads, w.page_size, w.head_dim, w.dtype)
     vp = sentinel_pool(w.num_pages, w.num_kv_heads, w.page_size, w.head_dim, w.dtype)
-    done, nbytes, busy = [], 0, 0.0
+    nbytes, busy = 0, 0.0
     ru0 = resource.getrusage(resource.RUSAGE_SELF)
-    for r in order.tolist():
+    for r in range(w.batch):
         d = w.request(r)
         t0 = time.perf_counter()
         o_paged.kv_write(kp, vp, d.k_cached, d.v_cached, w.cached_slots(r), w.page_size)
@@ -245,17 +248,37 @@ def cpu_baseline(seconds):
         o_attn.paged_decode(d.q, kp, vp, w.block_tables[r:r + 1], w.context_lens[r:r + 1],
                             w.scale, w.page_size, w.dtype)
         busy += time.perf_counter() - t0
-        done.append(r)
         nbytes += int(w.context_lens[r]) * w.num_kv_heads * w.head_dim * 2 * 2
-        if busy >= seconds:
-            break
     ru1 = resource.getrusage(resource.RUSAGE_SELF)
     cpu = (ru1.ru_utime - ru0.ru_utime) + (ru1.ru_stime - ru0.ru_stime)
     cores = max(1, int(round(cpu / max(busy, 1e-9))))
+    del kp, vp
+
+    w4 = make_workload(4)
+    kp = sentinel_pool(w4.num_pages, w4.num_kv_heads, w4.page_size, w4.head_dim, w4.dtype)
+    vp = sentinel_pool(w4.num_pages, w4.num_kv_heads, w4.page_size, w4.head_dim, w4.dtype)
+    pflops, pbusy, pdone = 0, 0.0, 0
+    for r in np.argsort(w4.new_lens).tolist():      # shortest chunks first
+        if pbusy >= max(1.0, seconds - busy):
+            break
+        d = w4.request(r)
+        t0 = time.perf_counter()
+        o_paged.kv_write(kp, vp, d.k_cached, d.v_cached, w4.cached_slots(r), w4.page_size)
+        o_paged.kv_write(kp, vp, d.k_new, d.v_new, w4.new_slots(r), w4.page_size)
+        o_attn.paged_attention(d.q, kp, vp, w4.block_tables[r:r + 1],
+                               np.array([0, int(w4.new_lens[r])]), w4.context_lens[r:r + 1],
+                               w4.scale, w4.page_size, w4.dtype)
+        pbusy += time.perf_counter() - t0
+        c, n = int(w4.cached_lens[r]), int(w4.new_lens[r])
+        pflops += (n * (c + 1) + n * (n - 1) // 2) * w4.num_q_heads * 4 * w4.head_dim
+        pdone += 1
     return dict(value=nbytes / busy / 1e9, unit="GB/s", cores=cores, kind="oracle",
-                sample=f"scatter write + fp64 decode of {len(done)} of the 256 decode-b256 "
-                       f"requests ({nbytes / 1e6:.0f} MB of K/V), {busy:.1f} s; "
-                       f"host has {len(os.sched_getaffinity(0))} usable cores")
+                sample=f"decode-b256 step, all {w.batch} requests (scatter write + fp64 decode over "
+                       f"{nbytes / 1e6:.0f} MB of K/V), {busy:.1f} s on the host; "
+                       f"{len(os.sched_getaffinity(0))} usable cores",
+                prefill={"value": pflops / max(pbusy, 1e-9) / 1e9, "unit": "GFLOP/s",
+                         "sample": f"{pdone} of {w4.batch} prefill-varlen requests (shortest chunks "
+                                   f"first), {pflops / 1e9:.1f} causal GFLOP in {pbusy:.1f} s"})
 
 
 def traffic_for(kernel_file, launches_bytes_key):
