@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--mixed-layers", type=int, default=2,
+                    help="layers of the Qwen3-8B-shaped mixed step to time (36 in the full model)")
     ap.add_argument("--calibrate", action="store_true",
                     help="time torch's copy and sum over 1 GiB (reference ceilings and the "
                          "plain copy kernel used to scale HBM byte counters), then exit")
@@ -102,6 +104,9 @@ def _pools(w, dev):
 
 
 class Inputs:
+    """A workload's inputs in HBM: pools (NaN sentinels) with the cached rows
+    written through the library, the new rows, q and the metadata."""
+
     def __init__(self, w, dev):
         import paged_kv_attention_16_amd as qil
         d = w.gather()
@@ -118,6 +123,38 @@ class Inputs:
         del d
 
 
+def timed_steps(segments, steps, warmup, flush, stream):
+    """Run `steps` timed steps; a step calls each segment in order.  Each
+    segment is bracketed by HIP events on `stream`; before each step the
+    flush buffer (if any) is rewritten.  Returns per-segment mean/median ms
+    and the mean step ms."""
+    import torch
+    for _ in range(warmup):
+        for f in segments:
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(segments) + 1)]
+          for _ in range(steps)]
+    for i in range(steps):
+        if flush is not None:
+            flush.fill_(float(i))
+        ev[i][0].record(stream)
+        for j, f in enumerate(segments):
+            f()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    seg = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(len(segments))] for e in ev])
+    step = np.array([e[0].elapsed_time(e[-1]) for e in ev])
+    return dict(mean=seg.mean(axis=0), median=np.median(seg, axis=0),
+                p10=np.percentile(seg, 10, axis=0), p90=np.percentile(seg, 90, axis=0),
+                step_mean=float(step.mean()))
+
+
+def write_bytes(w, tokens):
+    """Algorithmic bytes of a scatter write: read and write both rows."""
+    return tokens * w.num_kv_heads * w.head_dim * w.elem_bytes * 2 * 2 + 4 * tokens
+
+
 def gpu_legs(args):
     import torch
     import paged_kv_attention_16_amd as qil
@@ -128,10 +165,10 @@ def gpu_legs(args):
         __graft_entry__.build()
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush = None if args.no_flush else torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     res = {}
 
-    # ---- decode leg ------------------------------------------------------
+    # ---- decode leg (headline) -------------------------------------------
     w = make_workload(3)
     t0 = time.time()
     x = Inputs(w, dev)
@@ -150,41 +187,22 @@ def gpu_legs(args):
                          keys_per_split=args.keys_per_split, workspace=ws, stream=stream)
 
     kv_bytes = w.decode_kv_bytes()
-    write_bytes = int(w.new_lens.sum()) * w.num_kv_heads * w.head_dim * 2 * 2 * 2 + 4 * w.batch
-    step_bytes = kv_bytes + w.decode_io_bytes() + write_bytes
+    step_bytes = kv_bytes + w.decode_io_bytes() + write_bytes(w, w.batch)
     dec_bytes = kv_bytes + w.decode_io_bytes()
-
-    for _ in range(args.warmup):
-        write(); decode()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    for i in range(args.steps):
-        if not args.no_flush:
-            flush.fill_(float(i))
-        a, b, c = ev[i]
-        a.record(stream)
-        write()
-        b.record(stream)
-        decode()
-        c.record(stream)
-    torch.cuda.synchronize()
+    t = timed_steps([write, decode], args.steps, args.warmup, flush, stream)
     wall = time.perf_counter() - wall0
-    step_ms = np.array([a.elapsed_time(c) for a, b, c in ev])
-    dec_ms = np.array([b.elapsed_time(c) for a, b, c in ev])
     res["decode"] = dict(
-        workload=w, step_ms=float(step_ms.mean()), dec_ms=float(dec_ms.mean()),
-        dec_ms_median=float(np.median(dec_ms)), dec_ms_p10=float(np.percentile(dec_ms, 10)),
-        dec_ms_p90=float(np.percentile(dec_ms, 90)), step_bytes=step_bytes, dec_bytes=dec_bytes,
+        workload=w, step_ms=t["step_mean"], dec_ms=float(t["mean"][1]),
+        dec_ms_median=float(t["median"][1]), dec_ms_p10=float(t["p10"][1]),
+        dec_ms_p90=float(t["p90"][1]), step_bytes=step_bytes, dec_bytes=dec_bytes,
         kv_bytes=kv_bytes, wall_s=wall, setup_s=setup_s, workspace=need)
-    print(f"[bench] decode-b256: step {step_ms.mean()*1e3:.1f} us, decode {dec_ms.mean()*1e3:.1f} us "
-          f"({dec_bytes / (dec_ms.mean() * 1e-3) / 1e9:.0f} GB/s), setup {setup_s:.1f}s", flush=True)
+    print(f"[bench] decode-b256: step {t['step_mean']*1e3:.1f} us, decode {t['mean'][1]*1e3:.1f} us "
+          f"({dec_bytes / (t['mean'][1] * 1e-3) / 1e9:.0f} GB/s), setup {setup_s:.1f}s", flush=True)
     del x, ws
     torch.cuda.empty_cache()
 
-    # ---- prefill leg -----------------------------------------------------
+    # ---- prefill leg ---------------------------------------------------------
     if not args.skip_prefill:
         w4 = make_workload(4)
         x = Inputs(w4, dev)
@@ -198,30 +216,78 @@ def gpu_legs(args):
             qil.paged_prefill(x.out, x.q, x.kp, x.vp, x.bt, cu, x.ctx, maxq, maxk,
                               float(w4.scale), stream=stream)
 
-        for _ in range(args.warmup):
-            write4(); prefill()
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-               torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-        for i in range(args.steps):
-            if not args.no_flush:
-                flush.fill_(float(i))
-            a, b, c = ev[i]
-            a.record(stream)
-            write4()
-            b.record(stream)
-            prefill()
-            c.record(stream)
-        torch.cuda.synchronize()
-        pre_ms = np.array([b.elapsed_time(c) for a, b, c in ev])
-        st_ms = np.array([a.elapsed_time(c) for a, b, c in ev])
+        t = timed_steps([write4, prefill], args.steps, args.warmup, flush, stream)
         flops = w4.prefill_flops()
-        res["prefill"] = dict(workload=w4, pre_ms=float(pre_ms.mean()),
-                              pre_ms_median=float(np.median(pre_ms)), step_ms=float(st_ms.mean()),
-                              flops=flops)
-        print(f"[bench] prefill-varlen: prefill {pre_ms.mean()*1e3:.1f} us "
-              f"({flops / (pre_ms.mean() * 1e-3) / 1e12:.1f} TFLOP/s)", flush=True)
+        ntok = int(w4.new_lens.sum())
+        res["prefill"] = dict(workload=w4, pre_ms=float(t["mean"][1]),
+                              pre_ms_median=float(t["median"][1]), step_ms=t["step_mean"],
+                              flops=flops, write_ms=float(t["mean"][0]),
+                              write_bytes=write_bytes(w4, ntok), write_tokens=ntok)
+        print(f"[bench] prefill-varlen: prefill {t['mean'][1]*1e3:.1f} us "
+              f"({flops / (t['mean'][1] * 1e-3) / 1e12:.1f} TFLOP/s); chunk write {ntok} tokens "
+              f"{t['mean'][0]*1e3:.1f} us ({write_bytes(w4, ntok) / (t['mean'][0] * 1e-3) / 1e9:.0f} GB/s)",
+              flush=True)
         del x
+        torch.cuda.empty_cache()
+
+    # ---- mixed step (fused write + decode + prefill per layer) -----------
+    if args.mixed_layers > 0:
+        layers = []
+        t0 = time.time()
+        for layer in range(args.mixed_layers):
+            w5 = make_workload(5, layer)
+            x = Inputs(w5, dev)
+            qw, kw = w5.norm_weights()
+            x.table = torch.empty(w5.max_position, w5.head_dim, dtype=torch.float32, device=dev)
+            qil.rope_cos_sin(x.table, w5.theta, stream=stream)
+            x.q_out = torch.empty_like(x.q)
+            x.fuse = qil.QKNormRope(x.q, x.q_out, _to_dev(qw, dev), _to_dev(kw, dev),
+                                    _i32(w5.positions_new(), dev), x.table, eps=w5.eps)
+            x.q_dec = x.q_out[:64]
+            x.q_pre = x.q_out[64:]
+            x.out_dec = torch.empty_like(x.q_dec)
+            x.out_pre = torch.empty_like(x.q_pre)
+            x.bt_dec, x.bt_pre = x.bt[:64].contiguous(), x.bt[64:].contiguous()
+            x.ctx_dec, x.ctx_pre = x.ctx[:64].contiguous(), x.ctx[64:].contiguous()
+            x.cu_pre = _i32(w5.cu_seqlens(w5.prefill_idx), dev)
+            x.maxl_dec = int(w5.context_lens[:64].max())
+            x.maxl_pre = int(w5.context_lens[64:].max())
+            need = qil.paged_decode_workspace_size(64, w5.num_q_heads, w5.num_kv_heads, x.maxl_dec,
+                                                   w5.page_size, 0)
+            x.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            layers.append((w5, x))
+        torch.cuda.synchronize()
+        mixed_setup = time.time() - t0
+        segs = []
+        for w5, x in layers:
+            def fused(x=x):
+                qil.kv_write(x.k_new, x.v_new, x.kp, x.vp, x.slots, fuse=x.fuse, stream=stream)
+
+            def dec(x=x, w5=w5):
+                qil.paged_decode(x.out_dec, x.q_dec, x.kp, x.vp, x.bt_dec, x.ctx_dec, x.maxl_dec,
+                                 float(w5.scale), workspace=x.ws, stream=stream)
+
+            def pre(x=x, w5=w5):
+                qil.paged_prefill(x.out_pre, x.q_pre, x.kp, x.vp, x.bt_pre, x.cu_pre, x.ctx_pre,
+                                  512, x.maxl_pre, float(w5.scale), stream=stream)
+            segs += [fused, dec, pre]
+        t = timed_steps(segs, args.steps, args.warmup, flush, stream)
+        nl = len(layers)
+        m = t["mean"].reshape(nl, 3)
+        fused_bytes = sum(int(w5.new_lens.sum()) * (w5.num_q_heads + 2 * w5.num_kv_heads) * 256 * 2
+                          for w5, _ in layers) / nl
+        dec_bytes5 = sum(w5.decode_kv_bytes() + w5.decode_io_bytes() for w5, _ in layers) / nl
+        pre_flops5 = sum(w5.prefill_flops() for w5, _ in layers) / nl
+        layer_ms = t["step_mean"] / nl
+        res["mixed"] = dict(layers=nl, layer_ms=layer_ms, fused_ms=float(m[:, 0].mean()),
+                            dec_ms=float(m[:, 1].mean()), pre_ms=float(m[:, 2].mean()),
+                            fused_bytes=fused_bytes, dec_bytes=dec_bytes5, pre_flops=pre_flops5,
+                            setup_s=mixed_setup)
+        print(f"[bench] mixed-8b x{nl} layers: {layer_ms*1e3:.1f} us/layer "
+              f"(fused write {m[:,0].mean()*1e3:.1f} us, decode {m[:,1].mean()*1e3:.1f} us, "
+              f"prefill {m[:,2].mean()*1e3:.1f} us), setup {mixed_setup:.1f}s", flush=True)
+        del layers
+        torch.cuda.empty_cache()
     return res
 
 
@@ -368,6 +434,29 @@ def main():
             "step_us_mean": round(p["step_ms"] * 1e3, 2),
             "traffic": traffic_for("prefill.hip", "prefill-varlen"),
         }
+    if "prefill" in res:
+        p = res["prefill"]
+        line["kv_write"] = {
+            "workload": f"prefill-varlen chunk write, {p['write_tokens']} tokens x 8 KV heads, plain copy",
+            "bound": "hbm", "achieved": round(p["write_bytes"] / (p["write_ms"] * 1e-3) / 1e9, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(p["write_bytes"] / (p["write_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "launch_us_mean": round(p["write_ms"] * 1e3, 2), "algorithmic_bytes": int(p["write_bytes"])}
+    if "mixed" in res:
+        m = res["mixed"]
+        line["mixed_step"] = {
+            "workload": "mixed-8b: Hq 32 / Hkv 8, per layer fused Q/K RMSNorm+RoPE write of 2112 "
+                        "tokens, decode of 64 requests (context U[512,8192]), prefill of 4 x 512 "
+                        "over prefixes U[0,4096]; page 16",
+            "layers_timed": m["layers"], "us_per_layer": round(m["layer_ms"] * 1e3, 1),
+            "us_per_36_layer_step": round(m["layer_ms"] * 1e3 * 36, 1),
+            "tokens_per_s_36_layers": round((64 + 2048) / (m["layer_ms"] * 36 * 1e-3), 1),
+            "fused_write": {"us": round(m["fused_ms"] * 1e3, 2),
+                            "GB_per_s": round(m["fused_bytes"] / (m["fused_ms"] * 1e-3) / 1e9, 1)},
+            "decode": {"us": round(m["dec_ms"] * 1e3, 2),
+                       "GB_per_s": round(m["dec_bytes"] / (m["dec_ms"] * 1e-3) / 1e9, 1)},
+            "prefill": {"us": round(m["pre_ms"] * 1e3, 2),
+                        "TFLOP_per_s": round(m["pre_flops"] / (m["pre_ms"] * 1e-3) / 1e12, 1)}}
     if not args.skip_cpu:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)
