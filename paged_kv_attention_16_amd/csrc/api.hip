@@ -136,6 +136,8 @@ int qil_kv_write(const void* k, const void* v, int64_t k_token_stride, int64_t v
     return fail(QIL_EINVAL, "token strides must be multiples of 8 elements");
   if ((int64_t)num_pages * page_size > INT32_MAX)
     return fail(QIL_EINVAL, "num_pages*page_size exceeds the int32 slot range");
+  if ((int64_t)num_tokens * (hq_check + 2 * num_kv_heads) > (int64_t)1 << 30)
+    return fail(QIL_EINVAL, "num_tokens*heads exceeds 2^30 head rows per call");
 
   qil::KvWriteArgs a{k, v, k_token_stride, v_token_stride, k_cache, v_cache, slot_mapping,
                      num_tokens, num_kv_heads, log2_page_size(page_size), num_pages,

@@ -7,34 +7,45 @@
 // to bf16 after normalising, after the weight product and after rotating),
 // and its RotaryEmbedding block for the cos/sin table.
 //
-// The plain write is a bandwidth-bound copy: every thread moves one 16-byte
-// chunk of one (token, head) row, so a wavefront moves 4 (bf16) or 2 (fp32)
-// whole 128-element rows with fully coalesced 16-byte loads and stores.
+// The plain write is a bandwidth-bound copy: a thread moves one 16-byte chunk
+// of one (token, head) row, so a wavefront moves 4 (bf16) or 2 (fp32) whole
+// 128-element rows per instruction with coalesced 16-byte accesses.
 #include "device_common.h"
 #include "qil_internal.h"
 
 namespace qil {
 namespace {
 
-// One thread = one 16-byte chunk of one (token, kv head) row of K and of V.
-__global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a, int chunks_per_row,
-                                                       int64_t total) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int c = (int)(idx % chunks_per_row);
-  const int64_t row = idx / chunks_per_row;
-  const int g = (int)(row % a.num_kv_heads);
-  const int64_t t = row / a.num_kv_heads;
+// One thread moves one 16-byte chunk of one (token, kv head) row of K and of
+// V: C = row bytes / 16 consecutive threads cover a row.  The new rows are
+// read exactly once, so their loads are non-temporal (measured faster than
+// plain loads, and faster than several rows per thread); the stores stay
+// cached, since attention reads the rows back right after.  Indices are
+// 32-bit (rows = tokens x heads <= 2^30); pool offsets are 64-bit.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream16(const char* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <int C>
+__global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a, int rows) {
+  const int r = blockIdx.x * (256 / C) + threadIdx.x / C;
+  const int c = threadIdx.x % C;
+  if (r >= rows) return;
+  const int eb = C / 8;  // element bytes: 16 chunks of 8 bf16, 32 chunks of 4 fp32
+  const int t = r / a.num_kv_heads;
+  const int g = r - t * a.num_kv_heads;
   const int32_t slot = a.slots[t];
   const int64_t page = slot >> a.log2_page;
   if (slot < 0 || page >= a.num_pages) return;  // -1 = skip; out-of-range never touched
   const int64_t off = slot & ((1 << a.log2_page) - 1);
-  const int64_t row_bytes = (int64_t)kHeadDim * a.elem_bytes;
-  const int64_t dst = (((page * a.num_kv_heads + g) << a.log2_page) + off) * row_bytes + c * 16;
-  const int64_t src_k = (t * a.k_stride + (int64_t)g * kHeadDim) * a.elem_bytes + c * 16;
-  const int64_t src_v = (t * a.v_stride + (int64_t)g * kHeadDim) * a.elem_bytes + c * 16;
-  const uint4 kv = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k) + src_k);
-  const uint4 vv = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v) + src_v);
+  const int64_t dst = ((((page * a.num_kv_heads + g) << a.log2_page) + off) * kHeadDim) * eb + c * 16;
+  const uint4 kv = load_stream16(static_cast<const char*>(a.k) +
+                                 ((int64_t)t * a.k_stride + (int64_t)g * kHeadDim) * eb + c * 16);
+  const uint4 vv = load_stream16(static_cast<const char*>(a.v) +
+                                 ((int64_t)t * a.v_stride + (int64_t)g * kHeadDim) * eb + c * 16);
   *reinterpret_cast<uint4*>(static_cast<char*>(a.k_cache) + dst) = kv;
   *reinterpret_cast<uint4*>(static_cast<char*>(a.v_cache) + dst) = vv;
 }
@@ -44,14 +55,13 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a, int chunks
 // second half, and the RoPE partner of an element sits 8 lanes away.
 // Rows of a token: [0, Hq) are q heads, [Hq, Hq+Hkv) k heads, then v heads.
 __global__ __launch_bounds__(256) void kv_write_fused_kernel(KvWriteArgs a, FusedArgs f,
-                                                             int64_t total_rows) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t row = gid >> 4;
+                                                             int total_rows) {
+  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
   const int j = threadIdx.x & 15;
   if (row >= total_rows) return;  // whole 16-lane groups exit together
   const int rows_per_token = f.num_q_heads + 2 * a.num_kv_heads;
-  const int64_t t = row / rows_per_token;
-  const int kind_row = (int)(row % rows_per_token);
+  const int t = row / rows_per_token;
+  const int kind_row = row - t * rows_per_token;
 
   const bool is_q = kind_row < f.num_q_heads;
   const bool is_k = !is_q && kind_row < f.num_q_heads + a.num_kv_heads;
@@ -66,12 +76,12 @@ __global__ __launch_bounds__(256) void kv_write_fused_kernel(KvWriteArgs a, Fuse
 
   const uint16_t* src;
   if (is_q)
-    src = static_cast<const uint16_t*>(f.q) + t * f.q_stride + (int64_t)head * kHeadDim;
+    src = static_cast<const uint16_t*>(f.q) + (int64_t)t * f.q_stride + head * kHeadDim;
   else if (is_k)
-    src = static_cast<const uint16_t*>(a.k) + t * a.k_stride + (int64_t)head * kHeadDim;
+    src = static_cast<const uint16_t*>(a.k) + (int64_t)t * a.k_stride + head * kHeadDim;
   else
-    src = static_cast<const uint16_t*>(a.v) + t * a.v_stride + (int64_t)head * kHeadDim;
-  const uint4 raw = *reinterpret_cast<const uint4*>(src + 8 * j);
+    src = static_cast<const uint16_t*>(a.v) + (int64_t)t * a.v_stride + head * kHeadDim;
+  const uint4 raw = load_stream16(reinterpret_cast<const char*>(src + 8 * j));
 
   if (!is_q && !is_k) {  // v: raw copy
     if (store_kv)
@@ -129,7 +139,8 @@ __global__ __launch_bounds__(256) void kv_write_fused_kernel(KvWriteArgs a, Fuse
   }
   const uint4 outv = {o32[0], o32[1], o32[2], o32[3]};
   if (is_q) {
-    uint16_t* dst = static_cast<uint16_t*>(f.q_out) + (t * f.num_q_heads + head) * kHeadDim + 8 * j;
+    uint16_t* dst =
+        static_cast<uint16_t*>(f.q_out) + ((int64_t)t * f.num_q_heads + head) * kHeadDim + 8 * j;
     *reinterpret_cast<uint4*>(dst) = outv;
   } else if (store_kv) {
     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.k_cache) + dst_row * kHeadDim + 8 * j) = outv;
@@ -152,17 +163,22 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float* table, int32_t m
 }  // namespace
 
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t s) {
-  const int chunks = kHeadDim * a.elem_bytes / 16;
-  const int64_t total = (int64_t)a.num_tokens * a.num_kv_heads * chunks;
-  const int64_t blocks = (total + 255) / 256;
-  hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, chunks, total);
+  const int rows = a.num_tokens * a.num_kv_heads;
+  if (a.elem_bytes == 2) {
+    const int per_block = 256 / 16;
+    hipLaunchKernelGGL(kv_write_kernel<16>, dim3((rows + per_block - 1) / per_block), dim3(256), 0, s,
+                       a, rows);
+  } else {
+    const int per_block = 256 / 32;
+    hipLaunchKernelGGL(kv_write_kernel<32>, dim3((rows + per_block - 1) / per_block), dim3(256), 0, s,
+                       a, rows);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_kv_write_fused(const KvWriteArgs& a, const FusedArgs& f, hipStream_t s) {
-  const int64_t rows = (int64_t)a.num_tokens * (f.num_q_heads + 2 * a.num_kv_heads);
-  const int64_t blocks = (rows * 16 + 255) / 256;
-  hipLaunchKernelGGL(kv_write_fused_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, f, rows);
+  const int rows = a.num_tokens * (f.num_q_heads + 2 * a.num_kv_heads);
+  hipLaunchKernelGGL(kv_write_fused_kernel, dim3((rows + 15) / 16), dim3(256), 0, s, a, f, rows);
   return hipGetLastError();
 }
 

@@ -58,6 +58,7 @@ def test_kv_write_validation(lib):
     assert kvw(lib, page=8) == EUNSUP
     assert kvw(lib, dtype=7) == EUNSUP
     assert kvw(lib, pages=0) == EINVAL
+    assert kvw(lib, T=2**27, hkv=8, ks=2048, vs=2048) == EINVAL  # 2^30 rows + 2^30 V rows
     assert "page_size" in lib.qil_last_error().decode() or True
     f = qil._QKNormRopeC(FAKE, FAKE, 4096, 32, FAKE, FAKE, 1e-6, FAKE, FAKE, 8192)
     assert kvw(lib, fuse=ctypes.pointer(f), dtype=0) == EUNSUP   # fused is bf16 only
