@@ -29,10 +29,14 @@
 //   * Online softmax in base 2 with a lazy reference maximum: the output is
 //     rescaled only when a row maximum grows by more than 2^8, so the weights
 //     exp2(s - m_ref) stay below 256 and most tiles skip the rescale.  The
-//     row sum adds the same rounded weights that feed the PV product.
+//     check runs once per 64-key tile, on the maximum of the whole tile and
+//     before any weight of the tile is formed, so every weight added to O
+//     and to the row sum is relative to the same reference.  The row sum
+//     adds the same rounded weights that feed the PV product.
 //   * Causal masking only on the diagonal band of tiles.
-//   * Each 64-key tile runs as two 32-key halves, ordered so that the
-//     exponentials of one half sit next to the matrix work of the other.
+//   * Each 64-key tile runs as two 32-key halves: the first half's row
+//     maximum sits next to the second half's QK^T matrix work, and the first
+//     half's PV product next to the second half's exponentials.
 // Block ids are laid out KV-head fastest, so with 8 KV heads all tiles of one
 // KV head land on one XCD (workgroups are dealt to the 8 XCDs round robin)
 // and its K/V stay in that XCD's L2.  Query tiles are issued last-first: the
@@ -240,17 +244,21 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int n_
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][s2], pb[s2], oacc[db], 0, 0, 0);
   };
 
-  // Row maximum of a half and the lazy rescale (a uniform branch, rarely taken).
-  auto max_half = [&](auto mask_tag, f32x16_t& s, int kbase) __attribute__((always_inline)) {
+  // Masked row maximum (raw scores) of a half.
+  auto half_max = [&](auto mask_tag, f32x16_t& s, int kbase, float& mx) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    float mx = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       if (MASK && kbase + acc_row(v, hf) > my_pos) s[v] = -INFINITY;
       mx = fmaxf(mx, s[v]);
     }
+  };
+  // The lazy rescale, once per tile before any weight of the tile is formed
+  // (a uniform branch, rarely taken).
+  auto rescale = [&](float mx) __attribute__((always_inline)) {
     mx = max_halves(mx) * qs;
     if (__ballot(mx > mref + kLazyRescale) != 0) {
+      asm volatile("" ::: "memory");  // keep the rare rescale a real branch
       const float mnew = fmaxf(mref, mx);
       const float corr = fast_exp2(mref - mnew);
       mref = mnew;
@@ -280,8 +288,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int n_
     }
   };
 
-  // One tile as two 32-key halves; each half's softmax sits next to the
-  // matrix work of the other half.
+  // One tile as two 32-key halves.
   auto compute = [&](auto mask_tag, int buf, int kt) __attribute__((always_inline)) {
     const int kbase = kt * kBN;
     bf16x8_t kop[8];
@@ -293,11 +300,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int n_
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     load_k(buf, 1, kop);
-    max_half(mask_tag, s0, kbase);
+    float mx = -INFINITY;
+    half_max(mask_tag, s0, kbase, mx);
     f32x16_t s1 = qk(kop);
+    half_max(mask_tag, s1, kbase + 32, mx);
+    rescale(mx);
     load_v(buf, 0, vop);
     exp_half(s0, p0);
-    max_half(mask_tag, s1, kbase + 32);
     pv(vop, p0);
     load_v(buf, 1, vop);
     exp_half(s1, p1);

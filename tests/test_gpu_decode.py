@@ -128,3 +128,25 @@ def test_fp32_ragged(qil):
     for split in (0, 64):
         got, ref = H.run_decode_case(w, DEV, keys_per_split=split)
         assert H.excess(got, ref, "f32") <= 0
+
+
+@pytest.mark.parametrize("split", [0, 64])
+def test_max_jumps_across_groups_and_splits(qil, split):
+    # Keys whose scores jump by ~10 in base 2 at several points of a long
+    # context: every running maximum, the cross-row and cross-wave merges and
+    # the split merge see large corrections.
+    from oracle import bf16 as obf
+    w = make_custom([1000, 300], [1, 1], hq=32, hkv=8, page=16, seed=41, decode=True)
+    d = w.gather()
+    kc = obf.bf16_to_f64(d["k_cached"]).astype(np.float32)
+    q = obf.bf16_to_f64(d["q"]).astype(np.float32)
+    for r0, n in ((0, 999), (999, 299)):   # cached rows of each request
+        for frac, mag in ((0.1, 10.0), (0.35, 30.0), (0.6, 50.0), (0.9, 70.0)):
+            kc[r0 + int(frac * n), :, 0] = mag
+    q[:, :, 0] = 4.0
+    d["k_cached"] = bf16_from_f32(kc)
+    d["q"] = bf16_from_f32(q)
+    case = H.DeviceCase(w, DEV, data=d)
+    got, ref = H.run_decode_case(w, DEV, keys_per_split=split, case=case)
+    print("spiked decode max abs err", np.max(np.abs(got - ref)), flush=True)
+    assert H.excess(got, ref, "bf16") <= 0

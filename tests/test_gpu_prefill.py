@@ -87,3 +87,41 @@ def test_run_twice_bitwise(qil):
     a = H.to_bits(case.prefill())
     b = H.to_bits(case.prefill())
     assert np.array_equal(a, b)
+
+
+def spiked_case(seed, hq=16, cached=0):
+    """One 300-token context (the first `cached` tokens already in the pool)
+    whose keys at positions 40, 105, 170 and 235 (each in the second 32-key
+    half of a 64-key tile) carry a growing component along dim 0, while every
+    query carries +4 there: each spike lifts the row maximum of the scores by
+    about 10 in base 2, past the kernels' 2^8 rescale threshold.  Values are
+    bf16 and finite."""
+    from workloads import bf16_from_f32
+    from oracle import bf16 as obf
+    w = make_custom([300], [300 - cached], hq=hq, hkv=8, page=16, seed=seed)
+    d = w.gather()
+    kc = obf.bf16_to_f64(d["k_cached"]).astype(np.float32)
+    kn = obf.bf16_to_f64(d["k_new"]).astype(np.float32)
+    q = obf.bf16_to_f64(d["q"]).astype(np.float32)
+    for pos, mag in ((40, 10.0), (105, 30.0), (170, 50.0), (235, 70.0)):
+        if pos < cached:
+            kc[pos, :, 0] = mag
+        else:
+            kn[pos - cached, :, 0] = mag
+    q[:, :, 0] = 4.0
+    d["k_cached"] = bf16_from_f32(kc)
+    d["k_new"] = bf16_from_f32(kn)
+    d["q"] = bf16_from_f32(q)
+    return w, d
+
+
+@pytest.mark.parametrize("hq,cached", [(16, 0), (32, 0), (64, 0), (16, 100)])
+def test_max_jump_inside_a_tile(qil, hq, cached):
+    # A row maximum that jumps inside the second half of a key tile must
+    # rescale everything accumulated before it, including the first half.
+    w, d = spiked_case(31, hq, cached)
+    case = H.DeviceCase(w, DEV, data=d)
+    got = H.to_f64(case.prefill())
+    ref = H.OracleCase(w, d, [0]).attention([0])
+    print(f"spiked prefill hq={hq} cached={cached} max abs err", np.max(np.abs(got - ref)), flush=True)
+    assert H.excess(got, ref, "bf16") <= 0
