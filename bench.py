@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--mixed-layers", type=int, default=2,
                     help="layers of the Qwen3-8B-shaped mixed step to time (36 in the full model)")
+    ap.add_argument("--graph-layers", type=int, default=28,
+                    help="layers of the decode step captured into a HIP graph per batch bucket "
+                         "(28 in Qwen3-0.6B; 0 skips the leg)")
     ap.add_argument("--calibrate", action="store_true",
                     help="time torch's copy and sum over 1 GiB (reference ceilings and the "
                          "plain copy kernel used to scale HBM byte counters), then exit")
@@ -310,7 +313,67 @@ def gpu_legs(args):
               f"prefill {m[:,2].mean()*1e3:.1f} us), setup {mixed_setup:.1f}s", flush=True)
         del layers
         torch.cuda.empty_cache()
+    if args.graph_layers > 0:
+        res["graph"] = graph_leg(args, dev, stream, flush)
     return res
+
+
+GRAPH_BUCKETS = (1, 2, 4, 8, 16, 32, 64, 128, 256)
+
+
+def graph_leg(args, dev, stream, flush):
+    """Decode step of `graph_layers` layers (write the new token's K/V, then
+    paged decode, per layer) at batch buckets 1 .. 256, issued eagerly from
+    Python and replayed as a HIP graph.  Contexts U[16,1024] + U[0,1024],
+    Hq 16 / Hkv 8, page 256, independent pools per layer with random page
+    placement; values are N(0,1) in bf16 (timing only: parity of the graph
+    path is a GPU test)."""
+    import torch
+    from paged_kv_attention_16_amd.graph import DecodeStepGraph
+    rng = np.random.default_rng(7)
+    B, hq, hkv, page, D = max(GRAPH_BUCKETS), 16, 8, 256, 128
+    ctx = (rng.integers(16, 1025, B) + rng.integers(0, 1025, B)).astype(np.int32)
+    need = -(-ctx // page)
+    num_pages = int(need.sum()) + 1
+    stride = int(need.max())
+    max_l = 2048
+    t0 = time.time()
+    # one page placement, shared by every layer's pools as in a real model
+    perm = rng.permutation(num_pages - 1).astype(np.int32) + 1   # page 0 is the pad page
+    bt = np.full((B, stride), -1, np.int32)
+    at = 0
+    for r, k in enumerate(need.tolist()):
+        bt[r, :k] = perm[at:at + k]
+        at += k
+    slots = (bt[np.arange(B), (ctx - 1) // page] * page + (ctx - 1) % page).astype(np.int32)
+    pools = []
+    for _ in range(args.graph_layers):
+        kp = torch.empty(num_pages, hkv, page, D, dtype=torch.bfloat16, device=dev).normal_()
+        pools.append((kp, torch.empty_like(kp).normal_()))
+    torch.cuda.synchronize()
+    setup = time.time() - t0
+    out = []
+    for bucket in GRAPH_BUCKETS:
+        g = DecodeStepGraph(pools, bucket, hq, stride, max_l, 0.08838834764831845, pad_page=0)
+        g.update(torch.from_numpy(slots[:bucket]).to(dev), torch.from_numpy(bt[:bucket]).to(dev),
+                 torch.from_numpy(ctx[:bucket]).to(dev),
+                 q=[torch.randn(bucket, hq, D, device=dev).to(torch.bfloat16) for _ in pools],
+                 k_new=[torch.randn(bucket, hkv, D, device=dev).to(torch.bfloat16) for _ in pools],
+                 v_new=[torch.randn(bucket, hkv, D, device=dev).to(torch.bfloat16) for _ in pools])
+        g.capture()
+        te = timed_steps([g.run_eager], args.steps, args.warmup, flush, stream)
+        tg = timed_steps([g.replay], args.steps, args.warmup, flush, stream)
+        eager_us, graph_us = te["step_mean"] * 1e3, tg["step_mean"] * 1e3
+        kv = int(ctx[:bucket].sum()) * hkv * D * 2 * 2 * len(pools)
+        out.append(dict(batch=bucket, eager_us=round(eager_us, 1), graph_us=round(graph_us, 1),
+                        launch_overhead_share=round(1 - graph_us / eager_us, 4),
+                        graph_GB_per_s=round(kv / (graph_us * 1e-6) / 1e9, 1)))
+        print(f"[bench] decode-graph B={bucket:3d}: eager {eager_us:8.1f} us, graph {graph_us:8.1f} us "
+              f"({100 * (1 - graph_us / eager_us):.1f}% launch overhead)", flush=True)
+        del g
+    del pools
+    torch.cuda.empty_cache()
+    return dict(layers=args.graph_layers, setup_s=setup, buckets=out)
 
 
 # ---- CPU baseline: the oracle, unchanged, on a bounded sample -------------
@@ -481,6 +544,13 @@ def main():
                        "GB_per_s": round(m["dec_bytes"] / (m["dec_ms"] * 1e-3) / 1e9, 1)},
             "prefill": {"us": round(m["pre_ms"] * 1e3, 2),
                         "TFLOP_per_s": round(m["pre_flops"] / (m["pre_ms"] * 1e-3) / 1e12, 1)}}
+    if "graph" in res:
+        gr = res["graph"]
+        line["decode_graph"] = {
+            "workload": f"decode step of {gr['layers']} layers (write 1 new token + paged decode per "
+                        "layer), Hq 16 / Hkv 8, page 256, context U[16,1024]+U[0,1024], "
+                        "eager Python launches vs HIP-graph replay per batch bucket",
+            "buckets": gr["buckets"]}
     if not args.skip_cpu:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)
