@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--graph-layers", type=int, default=28,
                     help="layers of the decode step captured into a HIP graph per batch bucket "
                          "(28 in Qwen3-0.6B; 0 skips the leg)")
+    ap.add_argument("--skip-shared", action="store_true",
+                    help="skip the shared-prefix leg (prefill and decode over a common prefix)")
     ap.add_argument("--calibrate", action="store_true",
                     help="time torch's copy and sum over 1 GiB (reference ceilings and the "
                          "plain copy kernel used to scale HBM byte counters), then exit")
@@ -315,7 +317,90 @@ def gpu_legs(args):
         torch.cuda.empty_cache()
     if args.graph_layers > 0:
         res["graph"] = graph_leg(args, dev, stream, flush)
+    if not args.skip_shared:
+        res["shared"] = shared_prefix_leg(args, dev, stream, flush)
     return res
+
+
+def shared_prefix_leg(args, dev, stream, flush):
+    """Requests over one common 4096-token prompt prefix held in 256 shared
+    read-only pages (prefix caching), against the same requests with private
+    copies of the prefix.  Qwen3-8B attention (Hq 32 / Hkv 8), page 16.
+      prefill: 8 requests, each a 512-token chunk after the prefix
+      decode:  64 requests, each one token after the prefix plus a private
+               tail of U[0, 1024] tokens
+    Timing only (N(0,1) bf16 pool values); parity is a GPU test."""
+    import torch
+    import paged_kv_attention_16_amd as qil
+    rng = np.random.default_rng(11)
+    hq, hkv, page, D, pre_pages = 32, 8, 16, 128, 256
+    scale = 0.08838834764831845
+
+    def tables(tails, shared):
+        B = len(tails)
+        tail_pages = -(-np.asarray(tails) // page)
+        n_pages = (pre_pages if shared else B * pre_pages) + int(tail_pages.sum())
+        perm = rng.permutation(n_pages).astype(np.int32)
+        bt = np.full((B, pre_pages + int(tail_pages.max())), -1, np.int32)
+        at = 0
+        if shared:
+            common = perm[:pre_pages]
+            at = pre_pages
+        for r in range(B):
+            if shared:
+                bt[r, :pre_pages] = common
+            else:
+                bt[r, :pre_pages] = perm[at:at + pre_pages]
+                at += pre_pages
+            bt[r, pre_pages:pre_pages + tail_pages[r]] = perm[at:at + tail_pages[r]]
+            at += tail_pages[r]
+        kp = torch.empty(n_pages, hkv, page, D, dtype=torch.bfloat16, device=dev).normal_()
+        return kp, torch.empty_like(kp).normal_(), torch.from_numpy(bt).to(dev)
+
+    out = {}
+    # prefill: 8 chunks of 512 after the shared prefix
+    tails = np.full(8, 512)
+    ctx = torch.from_numpy((pre_pages * page + tails).astype(np.int32)).to(dev)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(tails)]).astype(np.int32)).to(dev)
+    q = torch.randn(int(tails.sum()), hq, D, device=dev).to(torch.bfloat16)
+    o = torch.empty_like(q)
+    maxk = int(pre_pages * page + tails.max())
+    pairs = sum(sum(pre_pages * page + i + 1 for i in range(n)) for n in tails.tolist())
+    flops = pairs * hq * 512
+    for shared in (True, False):
+        kp, vp, bt = tables(tails, shared)
+        t = timed_steps([lambda: qil.paged_prefill(o, q, kp, vp, bt, cu, ctx, 512, maxk, scale,
+                                                   stream=stream)], args.steps, args.warmup, flush, stream)
+        key = "prefill_shared" if shared else "prefill_private"
+        out[key] = dict(us=round(t["step_mean"] * 1e3, 2),
+                        TFLOP_per_s=round(flops / (t["step_mean"] * 1e-3) / 1e12, 1))
+        del kp, vp, bt
+    # decode: 64 requests, prefix + private tail, one query token each
+    tails = rng.integers(1, 1025, 64)
+    ctx_np = (pre_pages * page + tails).astype(np.int32)
+    ctx = torch.from_numpy(ctx_np).to(dev)
+    q = torch.randn(64, hq, D, device=dev).to(torch.bfloat16)
+    o = torch.empty_like(q)
+    maxl = int(ctx_np.max())
+    need = qil.paged_decode_workspace_size(64, hq, hkv, maxl, page, 0)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    algo = int(ctx_np.sum()) * hkv * D * 2 * 2
+    unique = (pre_pages * page + int(tails.sum())) * hkv * D * 2 * 2
+    for shared in (True, False):
+        kp, vp, bt = tables(tails, shared)
+        t = timed_steps([lambda: qil.paged_decode(o, q, kp, vp, bt, ctx, maxl, scale, workspace=ws,
+                                                  stream=stream)], args.steps, args.warmup, flush, stream)
+        key = "decode_shared" if shared else "decode_private"
+        out[key] = dict(us=round(t["step_mean"] * 1e3, 2),
+                        context_GB_per_s=round(algo / (t["step_mean"] * 1e-3) / 1e9, 1))
+        if shared:
+            out[key]["unique_GB_per_s"] = round(unique / (t["step_mean"] * 1e-3) / 1e9, 1)
+        del kp, vp, bt
+    torch.cuda.empty_cache()
+    print(f"[bench] shared-prefix: prefill {out['prefill_shared']['TFLOP_per_s']} vs "
+          f"{out['prefill_private']['TFLOP_per_s']} TFLOP/s (shared vs private), decode "
+          f"{out['decode_shared']['us']} vs {out['decode_private']['us']} us", flush=True)
+    return out
 
 
 GRAPH_BUCKETS = (1, 2, 4, 8, 16, 32, 64, 128, 256)
@@ -551,6 +636,12 @@ def main():
                         "layer), Hq 16 / Hkv 8, page 256, context U[16,1024]+U[0,1024], "
                         "eager Python launches vs HIP-graph replay per batch bucket",
             "buckets": gr["buckets"]}
+    if "shared" in res:
+        line["shared_prefix"] = {
+            "workload": "Hq 32 / Hkv 8, page 16, a 4096-token prefix in 256 shared pages vs "
+                        "private copies; prefill: 8 chunks of 512 after it; decode: 64 requests "
+                        "with private tails U[1,1024]",
+            **res["shared"]}
     if not args.skip_cpu:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)
