@@ -573,7 +573,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "qil_paged_decode (decode_split_kernel + decode_merge_kernel)",
+            "kernel": "qil_paged_decode (decode_mfma_kernel<2>; one split per request, no merge pass)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -71,7 +71,7 @@ def test_kv_write_validation(lib):
 
 
 def dec(lib, **kw):
-    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, bts=128, ctx=FAKE, B=32, hq=16, hkv=8,
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, bts=128, ctx=FAKE, B=2, hq=16, hkv=8,
              d=128, page=16, pages=8192, maxL=2048, scale=0.088, dtype=1, S=0, ws=None, wsb=0)
     a.update(kw)
     return lib.qil_paged_decode(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["bts"], a["ctx"],
@@ -80,10 +80,12 @@ def dec(lib, **kw):
 
 
 def test_decode_validation(lib):
-    need = lib.qil_paged_decode_workspace_size(32, 16, 8, 2048, 16, 0)
+    # 2 requests x 8 KV heads over up to 2048 keys: the plan splits (256 keys)
+    need = lib.qil_paged_decode_workspace_size(2, 16, 8, 2048, 16, 0)
     assert need > 0
     assert lib.qil_paged_decode_workspace_size(1, 16, 8, 64, 16, 0) == 0   # one split: none
-    assert lib.qil_paged_decode_workspace_size(32, 16, 8, 2048, 16, 4096) == 0
+    assert lib.qil_paged_decode_workspace_size(32, 16, 8, 2048, 16, 0) == 0  # one split per request
+    assert lib.qil_paged_decode_workspace_size(2, 16, 8, 2048, 16, 4096) == 0
     assert dec(lib, B=0) == 0
     assert dec(lib) == EWS                          # workspace missing
     assert dec(lib, ws=FAKE, wsb=need - 1) == EWS
