@@ -31,11 +31,23 @@
  *  - dtype: QIL_F32 (IEEE binary32) or QIL_BF16 (bfloat16).  Outputs have the
  *    input dtype; accumulation is fp32.  Pointers must be 16-byte aligned.
  *  - Device-resident metadata (slots, page ids, lengths) is a precondition,
- *    not checked.  The kernels still never dereference an out-of-range page
- *    id or slot and never read a block-table row past max_context_len: a
- *    write to such a slot is skipped, and the attention output of a request
- *    whose table holds such a page is unspecified (but finite memory is all
- *    that is touched).
+ *    not checked by default.  The kernels still never dereference an
+ *    out-of-range page id or slot and never read a block-table row past
+ *    max_context_len: a write to such a slot is skipped, and the attention
+ *    output of a request whose table holds such a page is unspecified (but
+ *    finite memory is all that is touched).
+ *  - Debug mode (environment variable QIL_DEBUG set to anything but "0" when
+ *    the library first looks, or qil_set_debug(1)) checks that metadata on
+ *    the device before each launch and returns QIL_EINVAL, with the first
+ *    violation in qil_last_error(), instead of launching: slots that are
+ *    neither -1 nor in the pool, duplicate slots within one kv_write call,
+ *    positions outside [0, max_position), context lengths outside
+ *    [1, min(max_context_len, block_table_stride*page_size)], block-table
+ *    entries that a request reads and that are not pages of the pool, and
+ *    cu_seqlens that do not run 0 <= ... <= total_q or give a request more
+ *    new tokens than its context or max_seqlen_q.  The checks synchronize
+ *    the stream, so debug-mode calls cannot be captured into a graph (they
+ *    return QIL_EINVAL under capture).
  *
  * KV pool layout (the "paged KV cache")
  * -------------------------------------
@@ -83,6 +95,11 @@ const char* qil_version(void);
 
 /* Description of the last error on the calling thread ("" if none). */
 const char* qil_last_error(void);
+
+/* Debug mode (see above): on (non-zero) or off for every later call in the
+ * process, overriding QIL_DEBUG.  qil_debug_enabled() reports the setting. */
+void qil_set_debug(int enabled);
+int qil_debug_enabled(void);
 
 /*
  * Fused per-head Q/K RMSNorm + RoPE applied by qil_kv_write before the

@@ -19,7 +19,7 @@ import os
 
 __all__ = [
     "QilError", "lib_path", "load", "version", "kv_write", "QKNormRope", "rope_cos_sin",
-    "paged_decode", "paged_decode_workspace_size", "paged_prefill",
+    "paged_decode", "paged_decode_workspace_size", "paged_prefill", "set_debug", "debug_enabled",
     "QIL_F32", "QIL_BF16",
 ]
 
@@ -67,6 +67,9 @@ def load(path=None):
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     lib.qil_version.restype = ctypes.c_char_p
     lib.qil_last_error.restype = ctypes.c_char_p
+    lib.qil_set_debug.restype = None
+    lib.qil_set_debug.argtypes = [ctypes.c_int]
+    lib.qil_debug_enabled.restype = ctypes.c_int
     lib.qil_kv_write.restype = ctypes.c_int
     lib.qil_kv_write.argtypes = [vp, vp, i64, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                  ctypes.POINTER(_QKNormRopeC), vp]
@@ -87,6 +90,16 @@ def load(path=None):
 
 def version():
     return load().qil_version().decode()
+
+
+def set_debug(enabled):
+    """Debug mode: check slots, positions, block tables, context lengths and
+    cu_seqlens on the device before each launch (synchronizes the stream)."""
+    load().qil_set_debug(1 if enabled else 0)
+
+
+def debug_enabled():
+    return bool(load().qil_debug_enabled())
 
 
 def _check(rc):

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqil.so")
 ARCH = os.environ.get("QIL_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.hip", "kv_write.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.hip", "kv_write.hip", "decode.hip", "prefill.hip", "debug_check.hip"]
 
 
 def hipcc():

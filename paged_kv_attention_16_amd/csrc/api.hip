@@ -8,6 +8,9 @@
 // cache pools and the slot mapping).
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
+
+#include <atomic>
 
 #include <hip/hip_runtime.h>
 
@@ -32,6 +35,76 @@ int ok() {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---- debug mode: check the device-resident metadata before each launch ----
+std::atomic<int> g_debug{-1};  // -1: not yet read from QIL_DEBUG
+
+bool debug_on() {
+  int d = g_debug.load(std::memory_order_relaxed);
+  if (d < 0) {
+    const char* env = getenv("QIL_DEBUG");
+    d = (env && env[0] && !(env[0] == '0' && env[1] == '\0')) ? 1 : 0;
+    int expected = -1;
+    g_debug.compare_exchange_strong(expected, d);
+    d = g_debug.load();
+  }
+  return d > 0;
+}
+
+int describe(const qil::DebugReport& r) {
+  switch (r.code) {
+    case qil::kBadSlot:
+      return fail(QIL_EINVAL, "QIL_DEBUG: slot_mapping[%d] = %d is neither -1 nor a slot of the pool",
+                  r.i, r.value);
+    case qil::kDuplicateSlot:
+      return fail(QIL_EINVAL, "QIL_DEBUG: slot_mapping[%d] and slot_mapping[%d] are both %d", r.i,
+                  r.j, r.value);
+    case qil::kBadPosition:
+      return fail(QIL_EINVAL, "QIL_DEBUG: positions[%d] = %d is outside [0, max_position)", r.i,
+                  r.value);
+    case qil::kBadContext:
+      return fail(QIL_EINVAL,
+                  "QIL_DEBUG: context_lens[%d] = %d is outside [1, min(max_context_len, "
+                  "block_table_stride*page_size)]",
+                  r.i, r.value);
+    case qil::kBadPage:
+      return fail(QIL_EINVAL, "QIL_DEBUG: block_tables[%d][%d] = %d is not a page of the pool", r.i,
+                  r.j, r.value);
+    case qil::kBadCuSeqlens:
+      return fail(QIL_EINVAL,
+                  "QIL_DEBUG: cu_seqlens_q[%d] = %d breaks 0 = cu[0] <= ... <= cu[batch] = total_q",
+                  r.i, r.value);
+    case qil::kChunkTooLong:
+      return fail(QIL_EINVAL, "QIL_DEBUG: request %d has %d new tokens but context_len %d", r.i,
+                  r.j, r.value);
+    case qil::kChunkAboveMax:
+      return fail(QIL_EINVAL, "QIL_DEBUG: request %d has %d new tokens, above max_seqlen_q %d",
+                  r.i, r.j, r.value);
+    default:
+      return fail(QIL_EINVAL, "QIL_DEBUG: metadata check failed (code %d)", r.code);
+  }
+}
+
+// Run the check kernels `enqueue` adds, wait for them, and turn the first
+// violation into QIL_EINVAL.  This synchronizes `s`, so it refuses to run
+// while the stream is being captured into a graph.
+template <class F>
+int run_checks(hipStream_t s, F enqueue) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(s, &cap);
+  if (e != hipSuccess) return fail(QIL_EHIP, "QIL_DEBUG: %s", hipGetErrorString(e));
+  if (cap != hipStreamCaptureStatusNone)
+    return fail(QIL_EINVAL, "QIL_DEBUG checks synchronize the stream; they cannot run under capture");
+  qil::DebugReport* rep = nullptr;
+  e = qil::debug_report_ptr(&rep);
+  if (e == hipSuccess) e = qil::launch_debug_clear(rep, s);
+  if (e == hipSuccess) e = enqueue(rep);
+  qil::DebugReport host{};
+  if (e == hipSuccess) e = hipMemcpyAsync(&host, rep, sizeof(host), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(QIL_EHIP, "QIL_DEBUG: %s", hipGetErrorString(e));
+  return host.code ? describe(host) : QIL_OK;
+}
 
 int log2_page_size(int32_t page_size) {
   switch (page_size) {
@@ -118,6 +191,10 @@ const char* qil_version(void) { return "qil 0.1.0 gfx950"; }
 
 const char* qil_last_error(void) { return g_err; }
 
+void qil_set_debug(int enabled) { g_debug.store(enabled ? 1 : 0); }
+
+int qil_debug_enabled(void) { return debug_on() ? 1 : 0; }
+
 int qil_kv_write(const void* k, const void* v, int64_t k_token_stride, int64_t v_token_stride,
                  void* k_cache, void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,
                  int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t num_pages,
@@ -147,7 +224,14 @@ int qil_kv_write(const void* k, const void* v, int64_t k_token_stride, int64_t v
                      num_tokens, num_kv_heads, log2_page_size(page_size), num_pages,
                      dtype == QIL_BF16 ? 2 : 4};
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t num_slots = (int64_t)num_pages * page_size;
   if (!fuse) {
+    if (debug_on()) {
+      rc = run_checks(s, [&](qil::DebugReport* rep) {
+        return qil::launch_check_slots(slot_mapping, num_tokens, num_slots, rep, s);
+      });
+      if (rc) return rc;
+    }
     hipError_t e = qil::launch_kv_write(a, s);
     if (e != hipSuccess) return fail(QIL_EHIP, "kv_write launch: %s", hipGetErrorString(e));
     return ok();
@@ -170,6 +254,15 @@ int qil_kv_write(const void* k, const void* v, int64_t k_token_stride, int64_t v
   qil::FusedArgs f{fuse->q, fuse->q_out, fuse->q_token_stride, fuse->num_q_heads,
                    fuse->q_norm_weight, fuse->k_norm_weight, fuse->eps, fuse->positions,
                    fuse->cos_sin, fuse->max_position};
+  if (debug_on()) {
+    rc = run_checks(s, [&](qil::DebugReport* rep) {
+      hipError_t e = qil::launch_check_slots(slot_mapping, num_tokens, num_slots, rep, s);
+      if (e == hipSuccess) e = qil::launch_check_positions(fuse->positions, num_tokens,
+                                                            fuse->max_position, rep, s);
+      return e;
+    });
+    if (rc) return rc;
+  }
   hipError_t e = qil::launch_kv_write_fused(a, f, s);
   if (e != hipSuccess) return fail(QIL_EHIP, "fused kv_write launch: %s", hipGetErrorString(e));
   return ok();
@@ -258,7 +351,15 @@ int qil_paged_decode(void* out, const void* q, const void* k_cache, const void* 
     a.ws_m = reinterpret_cast<float*>(base + up(parts * qil::kHeadDim * 4));
     a.ws_l = reinterpret_cast<float*>(base + up(parts * qil::kHeadDim * 4) + up(parts * 4));
   }
-  hipError_t e = qil::launch_decode(a, static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_on()) {
+    rc = run_checks(s, [&](qil::DebugReport* rep) {
+      return qil::launch_check_tables(block_tables, block_table_stride, context_lens, batch,
+                                      a.log2_page, num_pages, max_context_len, rep, s);
+    });
+    if (rc) return rc;
+  }
+  hipError_t e = qil::launch_decode(a, s);
   if (e != hipSuccess) return fail(QIL_EHIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -294,7 +395,19 @@ int qil_paged_prefill(void* out, const void* q, const void* k_cache, const void*
   qil::PrefillArgs a{out, q, k_cache, v_cache, block_tables, block_table_stride, cu_seqlens_q,
                      context_lens, batch, total_q, max_seqlen_q, max_context_len, num_q_heads,
                      num_kv_heads, log2_page_size(page_size), num_pages, scale};
-  hipError_t e = qil::launch_prefill(a, static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_on()) {
+    rc = run_checks(s, [&](qil::DebugReport* rep) {
+      hipError_t e = qil::launch_check_cu(cu_seqlens_q, context_lens, batch, total_q,
+                                          max_seqlen_q, rep, s);
+      if (e == hipSuccess)
+        e = qil::launch_check_tables(block_tables, block_table_stride, context_lens, batch,
+                                     a.log2_page, num_pages, max_context_len, rep, s);
+      return e;
+    });
+    if (rc) return rc;
+  }
+  hipError_t e = qil::launch_prefill(a, s);
   if (e != hipSuccess) return fail(QIL_EHIP, "prefill launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -94,3 +94,39 @@ struct PrefillArgs {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 
 }  // namespace qil
+
+// ---- debug checks of device-resident metadata --------------------------------
+namespace qil {
+
+// First violation found by a check kernel (code 0 = none).
+struct DebugReport {
+  int32_t code;
+  int32_t i, j, value;
+};
+
+enum DebugCode : int32_t {
+  kBadSlot = 1,       // i = token, value = slot
+  kDuplicateSlot = 2, // i < j tokens, value = slot
+  kBadPosition = 3,   // i = token, value = position
+  kBadContext = 4,    // i = request, value = context length
+  kBadPage = 5,       // i = request, j = block-table column, value = page id
+  kBadCuSeqlens = 6,  // i = index into cu_seqlens, value = entry
+  kChunkTooLong = 7,  // i = request, j = new tokens, value = context length
+  kChunkAboveMax = 8, // i = request, j = new tokens, value = max_seqlen_q
+};
+
+// Device address of this device's report (resolved once per device).
+hipError_t debug_report_ptr(DebugReport** ptr);
+hipError_t launch_debug_clear(DebugReport* rep, hipStream_t s);
+hipError_t launch_check_slots(const int32_t* slots, int32_t n, int64_t num_slots,
+                              DebugReport* rep, hipStream_t s);
+hipError_t launch_check_positions(const int32_t* pos, int32_t n, int32_t max_position,
+                                  DebugReport* rep, hipStream_t s);
+hipError_t launch_check_tables(const int32_t* block_tables, int32_t bt_stride,
+                               const int32_t* context_lens, int32_t batch, int32_t log2_page,
+                               int32_t num_pages, int32_t max_context_len, DebugReport* rep,
+                               hipStream_t s);
+hipError_t launch_check_cu(const int32_t* cu, const int32_t* context_lens, int32_t batch,
+                           int32_t total_q, int32_t max_seqlen_q, DebugReport* rep, hipStream_t s);
+
+}  // namespace qil

@@ -131,6 +131,15 @@ def test_rope_table_validation(lib):
     assert lib.qil_rope_cos_sin(FAKE, 10, 128, 0.5, None) == EINVAL
 
 
+def test_debug_switch(lib):
+    was = lib.qil_debug_enabled()
+    lib.qil_set_debug(1)
+    assert lib.qil_debug_enabled() == 1
+    lib.qil_set_debug(0)
+    assert lib.qil_debug_enabled() == 0
+    lib.qil_set_debug(was)
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(qil.QilError):
         qil.load(str(tmp_path / "missing.so"))
