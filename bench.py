@@ -193,6 +193,8 @@ def gpu_legs(args):
     flush = None if args.no_flush else torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     res = {}
 
+    res["ceilings"] = measured_ceilings(dev, stream)
+
     # ---- decode leg (headline) -------------------------------------------
     w = make_workload(3)
     t0 = time.time()
@@ -406,6 +408,44 @@ def shared_prefix_leg(args, dev, stream, flush):
 GRAPH_BUCKETS = (1, 2, 4, 8, 16, 32, 64, 128, 256)
 
 
+def measured_ceilings(dev, stream):
+    """What plain kernels reach on this GPU: a non-temporal streaming read of
+    2 GiB (best of 1024 / 2048 / 4096 workgroups) and a loop of independent
+    bf16 32x32x16 MFMAs on every SIMD.  The secondary roofline denominators."""
+    import ctypes
+    import torch
+    from paged_kv_attention_16_amd import build as qbuild
+    lib = ctypes.CDLL(qbuild.CEILING_LIB)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    lib.qil_ceiling_stream_read.argtypes = [vp, sz, vp, i32, vp]
+    lib.qil_ceiling_mfma_bf16.argtypes = [vp, i32, i32, vp]
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(256, dtype=torch.float32, device=dev)
+    s = ctypes.c_void_p(stream.cuda_stream)
+    best = 0.0
+    for blocks in (1024, 2048, 4096):
+        def rd():
+            rc = lib.qil_ceiling_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                             ctypes.c_void_p(sink.data_ptr()), blocks, s)
+            assert rc == 0, rc
+        t = timed_steps([rd], 5, 2, None, stream)
+        best = max(best, nbytes / (t["step_mean"] * 1e-3) / 1e9)
+    del buf
+    blocks, iters = 1024, 20000
+
+    def mm():
+        rc = lib.qil_ceiling_mfma_bf16(ctypes.c_void_p(sink.data_ptr()), blocks, iters, s)
+        assert rc == 0, rc
+    t = timed_steps([mm], 3, 1, None, stream)
+    flops = blocks * 4 * 4 * iters * 32768
+    tf = flops / (t["step_mean"] * 1e-3) / 1e12
+    torch.cuda.empty_cache()
+    print(f"[bench] measured ceilings: stream read {best:.0f} GB/s, bf16 MFMA {tf:.0f} TFLOP/s",
+          flush=True)
+    return dict(stream_read_GB_s=round(best, 1), mfma_bf16_TFLOP_s=round(tf, 1))
+
+
 def graph_leg(args, dev, stream, flush):
     """Decode step of `graph_layers` layers (write the new token's K/V, then
     paged decode, per layer) at batch buckets 1 .. 256, issued eagerly from
@@ -585,6 +625,8 @@ def main():
                              "separately bracketed write",
             "event_bracket_us_mean": round(dec["dec_bracket_ms"] * 1e3, 2),
             "event_bracket_us_median": round(dec["dec_bracket_ms_median"] * 1e3, 2),
+            "measured_ceiling": res["ceilings"]["stream_read_GB_s"],
+            "frac_of_measured": round(achieved / res["ceilings"]["stream_read_GB_s"], 4),
         },
         "decode_tokens_per_s": round(w.batch / (dec["step_ms"] * 1e-3), 1),
     }
@@ -605,6 +647,8 @@ def main():
             "event_bracket_us_median": round(p["pre_bracket_ms_median"] * 1e3, 2),
             "step_us_mean": round(p["step_ms"] * 1e3, 2),
             "traffic": traffic_for("prefill.hip", "prefill-varlen"),
+            "measured_ceiling": res["ceilings"]["mfma_bf16_TFLOP_s"],
+            "frac_of_measured": round(tf / res["ceilings"]["mfma_bf16_TFLOP_s"], 4),
         }
     if "prefill" in res:
         p = res["prefill"]

@@ -3,7 +3,8 @@
     python -m paged_kv_attention_16_amd.build
 
 Every source under csrc/ is compiled by hipcc in parallel into _build/, then
-linked into paged_kv_attention_16_amd/libqil.so.  The build always compiles;
+linked into paged_kv_attention_16_amd/libqil.so (the attention path) and
+libqil_ceiling.so (the benchmark's measured-ceiling kernels).  The build always compiles;
 it never reuses stale objects.
 """
 
@@ -21,6 +22,9 @@ LIB = os.path.join(PKG, "libqil.so")
 ARCH = os.environ.get("QIL_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["api.hip", "kv_write.hip", "decode.hip", "prefill.hip", "debug_check.hip"]
+# measured-ceiling kernels for the benchmark, in a library of their own
+CEILING_SOURCE = "ceiling.hip"
+CEILING_LIB = os.path.join(PKG, "libqil_ceiling.so")
 
 
 def hipcc():
@@ -53,18 +57,23 @@ def _compile(src):
     return obj
 
 
-def build(verbose=True):
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"link failed:\n{p.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose=True):
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(len(SOURCES) + 1) as ex:
+        objs = list(ex.map(_compile, SOURCES + [CEILING_SOURCE]))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], CEILING_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CEILING_LIB}")
     return LIB
 
 
