@@ -172,6 +172,7 @@ def timed_steps(segments, steps, warmup, flush, stream):
     return dict(mean=mean, median=np.median(seg, axis=0),
                 p10=np.percentile(seg, 10, axis=0), p90=np.percentile(seg, 90, axis=0),
                 step_mean=float(step.mean()), step_median=float(np.median(step)),
+                step_p10=float(np.percentile(step, 10)), step_p90=float(np.percentile(step, 90)),
                 last_ms=float(step.mean() - mean[:-1].sum()))
 
 
@@ -219,8 +220,12 @@ def gpu_legs(args):
     wall0 = time.perf_counter()
     t = timed_steps([write, decode], args.steps, args.warmup, flush, stream)
     wall = time.perf_counter() - wall0
+    # the same step with warm caches (no flush): a labelled secondary number
+    th = timed_steps([write, decode], args.steps, args.warmup, None, stream)
     res["decode"] = dict(
         workload=w, step_ms=t["step_mean"], dec_ms=t["last_ms"], dec_bracket_ms=float(t["mean"][1]),
+        step_ms_median=t["step_median"], step_ms_p10=t["step_p10"], step_ms_p90=t["step_p90"],
+        hot_dec_ms=th["last_ms"],
         dec_bracket_ms_median=float(t["median"][1]), write_ms=float(t["mean"][0]),
         step_bytes=step_bytes, dec_bytes=dec_bytes,
         kv_bytes=kv_bytes, wall_s=wall, setup_s=setup_s, workspace=need)
@@ -303,18 +308,35 @@ def gpu_legs(args):
         t = timed_steps(segs, args.steps, args.warmup, flush, stream)
         nl = len(layers)
         m = t["mean"].reshape(nl, 3)
+        # the same layers with decode and prefill in one launch per layer
+        segs1 = []
+        for i, (w5, x) in enumerate(layers):
+            x.dec_batch = dict(out=x.out_dec, q=x.q_dec, block_tables=x.bt_dec,
+                               context_lens=x.ctx_dec, max_context_len=x.maxl_dec, workspace=x.ws)
+            x.pre_batch = dict(out=x.out_pre, q=x.q_pre, block_tables=x.bt_pre,
+                               cu_seqlens_q=x.cu_pre, context_lens=x.ctx_pre, max_seqlen_q=512,
+                               max_context_len=x.maxl_pre)
+
+            def both(x=x, w5=w5):
+                qil.paged_attention_mixed(x.kp, x.vp, float(w5.scale), decode=x.dec_batch,
+                                          prefill=x.pre_batch, stream=stream)
+            segs1 += [segs[3 * i], both]   # the layer's fused write, then both batches
+        t1 = timed_steps(segs1, args.steps, args.warmup, flush, stream)
         fused_bytes = sum(int(w5.new_lens.sum()) * (w5.num_q_heads + 2 * w5.num_kv_heads) * 256 * 2
                           for w5, _ in layers) / nl
         dec_bytes5 = sum(w5.decode_kv_bytes() + w5.decode_io_bytes() for w5, _ in layers) / nl
         pre_flops5 = sum(w5.prefill_flops() for w5, _ in layers) / nl
         layer_ms = t["step_mean"] / nl
-        res["mixed"] = dict(layers=nl, layer_ms=layer_ms, fused_ms=float(m[:, 0].mean()),
+        res["mixed"] = dict(layers=nl, layer_ms=layer_ms, single_launch_layer_ms=t1["step_mean"] / nl,
+                            single_launch_ms=float(t1["mean"].reshape(nl, 2)[:, 1].mean()),
+                            fused_ms=float(m[:, 0].mean()),
                             dec_ms=float(m[:, 1].mean()), pre_ms=float(m[:, 2].mean()),
                             fused_bytes=fused_bytes, dec_bytes=dec_bytes5, pre_flops=pre_flops5,
                             setup_s=mixed_setup)
         print(f"[bench] mixed-8b x{nl} layers: {layer_ms*1e3:.1f} us/layer "
               f"(fused write {m[:,0].mean()*1e3:.1f} us, decode {m[:,1].mean()*1e3:.1f} us, "
-              f"prefill {m[:,2].mean()*1e3:.1f} us), setup {mixed_setup:.1f}s", flush=True)
+              f"prefill {m[:,2].mean()*1e3:.1f} us); decode + prefill in one launch: "
+              f"{t1['step_mean'] / nl * 1e3:.1f} us/layer; setup {mixed_setup:.1f}s", flush=True)
         del layers
         torch.cuda.empty_cache()
     if args.graph_layers > 0:
@@ -627,7 +649,10 @@ def main():
             "event_bracket_us_median": round(dec["dec_bracket_ms_median"] * 1e3, 2),
             "measured_ceiling": res["ceilings"]["stream_read_GB_s"],
             "frac_of_measured": round(achieved / res["ceilings"]["stream_read_GB_s"], 4),
+            "hot_no_flush_GB_s": round(dec["dec_bytes"] / (dec["hot_dec_ms"] * 1e-3) / 1e9, 1),
         },
+        "step_us": {"mean": round(dec["step_ms"] * 1e3, 2), "median": round(dec["step_ms_median"] * 1e3, 2),
+                    "p10": round(dec["step_ms_p10"] * 1e3, 2), "p90": round(dec["step_ms_p90"] * 1e3, 2)},
         "decode_tokens_per_s": round(w.batch / (dec["step_ms"] * 1e-3), 1),
     }
     if "prefill" in res:
@@ -665,6 +690,8 @@ def main():
                         "tokens, decode of 64 requests (context U[512,8192]), prefill of 4 x 512 "
                         "over prefixes U[0,4096]; page 16",
             "layers_timed": m["layers"], "us_per_layer": round(m["layer_ms"] * 1e3, 1),
+            "us_per_layer_single_launch": round(m["single_launch_layer_ms"] * 1e3, 1),
+            "single_launch_us": round(m["single_launch_ms"] * 1e3, 2),
             "us_per_36_layer_step": round(m["layer_ms"] * 1e3 * 36, 1),
             "tokens_per_s_36_layers": round((64 + 2048) / (m["layer_ms"] * 36 * 1e-3), 1),
             "fused_write": {"us": round(m["fused_ms"] * 1e3, 2),

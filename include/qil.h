@@ -221,6 +221,54 @@ int qil_paged_prefill(void* out, const void* q, const void* k_cache, const void*
                       int32_t page_size, int32_t num_pages, float scale, int32_t dtype,
                       void* stream);
 
+/*
+ * qil_paged_attention_mixed -- the decode batch and the prefill batch of one
+ * step in a single launch over the same KV pool (plus the decode split merge
+ * when the decode part has several splits).  The "qwen-engine" README keeps
+ * prefill (compute-bound) and decode (memory-bound) in separate batches; here
+ * they stay separate argument sets, with the meaning of qil_paged_decode and
+ * qil_paged_prefill above, but their workgroups share the GPU: prefill query
+ * tiles and decode splits are interleaved in one grid, so MFMA-bound and
+ * HBM-bound work run side by side and the step has one tail.  bf16 only.
+ *
+ *   decode   NULL or a decode batch; its workspace is sized by
+ *            qil_paged_decode_workspace_size (same split plan)
+ *   prefill  NULL or a prefill batch (its K/V rows already written)
+ * Both batches use k_cache / v_cache, the head counts, page size, scale and
+ * dtype given here.  Each batch's arguments are checked as in its own call
+ * (a NULL or empty batch is allowed); outputs must not overlap.
+ */
+typedef struct qil_decode_batch {
+  void* out;                       /* [batch][num_q_heads][head_dim] */
+  const void* q;                   /* [batch][num_q_heads][head_dim] */
+  const int32_t* block_tables;     /* [batch][block_table_stride]    */
+  int32_t block_table_stride;
+  const int32_t* context_lens;     /* [batch]                        */
+  int32_t batch;
+  int32_t max_context_len;
+  int32_t keys_per_split;          /* 0 = automatic                  */
+  void* workspace;
+  size_t workspace_bytes;
+} qil_decode_batch;
+
+typedef struct qil_prefill_batch {
+  void* out;                       /* [total_q][num_q_heads][head_dim] */
+  const void* q;                   /* [total_q][num_q_heads][head_dim] */
+  const int32_t* block_tables;     /* [batch][block_table_stride]      */
+  int32_t block_table_stride;
+  const int32_t* cu_seqlens_q;     /* [batch + 1]                      */
+  const int32_t* context_lens;     /* [batch]                          */
+  int32_t batch;
+  int32_t total_q;
+  int32_t max_seqlen_q;
+  int32_t max_context_len;
+} qil_prefill_batch;
+
+int qil_paged_attention_mixed(const qil_decode_batch* decode, const qil_prefill_batch* prefill,
+                              const void* k_cache, const void* v_cache, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                              int32_t num_pages, float scale, int32_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,7 +19,8 @@ import os
 
 __all__ = [
     "QilError", "lib_path", "load", "version", "kv_write", "QKNormRope", "rope_cos_sin",
-    "paged_decode", "paged_decode_workspace_size", "paged_prefill", "set_debug", "debug_enabled",
+    "paged_decode", "paged_decode_workspace_size", "paged_prefill", "paged_attention_mixed",
+    "set_debug", "debug_enabled",
     "QIL_F32", "QIL_BF16",
 ]
 
@@ -34,6 +35,25 @@ class QilError(RuntimeError):
     def __init__(self, code, message):
         super().__init__(f"qil error {code}: {message}")
         self.code = code
+
+
+class _DecodeBatchC(ctypes.Structure):
+    _fields_ = [
+        ("out", ctypes.c_void_p), ("q", ctypes.c_void_p), ("block_tables", ctypes.c_void_p),
+        ("block_table_stride", ctypes.c_int32), ("context_lens", ctypes.c_void_p),
+        ("batch", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
+        ("keys_per_split", ctypes.c_int32), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class _PrefillBatchC(ctypes.Structure):
+    _fields_ = [
+        ("out", ctypes.c_void_p), ("q", ctypes.c_void_p), ("block_tables", ctypes.c_void_p),
+        ("block_table_stride", ctypes.c_int32), ("cu_seqlens_q", ctypes.c_void_p),
+        ("context_lens", ctypes.c_void_p), ("batch", ctypes.c_int32), ("total_q", ctypes.c_int32),
+        ("max_seqlen_q", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
+    ]
 
 
 def lib_path():
@@ -80,6 +100,10 @@ def load(path=None):
     lib.qil_paged_decode.restype = ctypes.c_int
     lib.qil_paged_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
                                      i32, f32, i32, i32, vp, sz, vp]
+    lib.qil_paged_attention_mixed.restype = ctypes.c_int
+    lib.qil_paged_attention_mixed.argtypes = [ctypes.POINTER(_DecodeBatchC),
+                                              ctypes.POINTER(_PrefillBatchC), vp, vp, i32, i32,
+                                              i32, i32, i32, f32, i32, vp]
     lib.qil_paged_prefill.restype = ctypes.c_int
     lib.qil_paged_prefill.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                       i32, i32, i32, i32, f32, i32, vp]
@@ -217,4 +241,47 @@ def paged_prefill(out, q, k_cache, v_cache, block_tables, cu_seqlens_q, context_
         int(block_tables.shape[1]), _ptr(cu_seqlens_q), _ptr(context_lens), batch, total_q,
         int(max_seqlen_q), int(max_context_len), hq, hkv, d, page, num_pages, float(scale),
         _dtype_code(q), _stream(stream))
+    _check(rc)
+
+
+def paged_attention_mixed(k_cache, v_cache, scale, decode=None, prefill=None, stream=None):
+    """A decode batch and a prefill batch over the same pools in one launch.
+
+    decode:  dict(out, q, block_tables, context_lens, max_context_len,
+                  keys_per_split=0, workspace=None)   (as paged_decode)
+    prefill: dict(out, q, block_tables, cu_seqlens_q, context_lens,
+                  max_seqlen_q, max_context_len)      (as paged_prefill)
+    """
+    import torch
+    num_pages, hkv, page, d = _pool_shape(k_cache)
+    ref_q = (decode or prefill)["q"]
+    hq = int(ref_q.shape[1])
+    dptr = pptr = None
+    keep = []
+    if decode is not None:
+        q = decode["q"]
+        kps = int(decode.get("keys_per_split", 0))
+        need = paged_decode_workspace_size(int(q.shape[0]), hq, hkv, int(decode["max_context_len"]),
+                                           page, kps)
+        ws = decode.get("workspace")
+        if ws is None and need > 0:
+            ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        keep.append(ws)
+        dc = _DecodeBatchC(decode["out"].data_ptr(), q.data_ptr(), decode["block_tables"].data_ptr(),
+                           int(decode["block_tables"].shape[1]), decode["context_lens"].data_ptr(),
+                           int(q.shape[0]), int(decode["max_context_len"]), kps,
+                           None if ws is None else ws.data_ptr(),
+                           0 if ws is None else ws.numel() * ws.element_size())
+        dptr = ctypes.pointer(dc)
+    if prefill is not None:
+        q = prefill["q"]
+        pc = _PrefillBatchC(prefill["out"].data_ptr(), q.data_ptr(), prefill["block_tables"].data_ptr(),
+                            int(prefill["block_tables"].shape[1]), prefill["cu_seqlens_q"].data_ptr(),
+                            prefill["context_lens"].data_ptr(), int(prefill["context_lens"].shape[0]),
+                            int(q.shape[0]), int(prefill["max_seqlen_q"]),
+                            int(prefill["max_context_len"]))
+        pptr = ctypes.pointer(pc)
+    rc = load().qil_paged_attention_mixed(dptr, pptr, _ptr(k_cache), _ptr(v_cache), hq, hkv, d,
+                                          page, num_pages, float(scale), _dtype_code(ref_q),
+                                          _stream(stream))
     _check(rc)

@@ -183,6 +183,128 @@ size_t workspace_bytes_for(int32_t batch, int32_t num_q_heads, const SplitPlan& 
   return up(parts * qil::kHeadDim * 4) + 2 * up(parts * 4);
 }
 
+hipError_t check_decode_metadata(const qil::DecodeArgs& a, qil::DebugReport* rep, hipStream_t s) {
+  return qil::launch_check_tables(a.block_tables, a.bt_stride, a.context_lens, a.batch, a.log2_page,
+                                  a.num_pages, a.max_context_len, rep, s);
+}
+
+hipError_t check_prefill_metadata(const qil::PrefillArgs& a, qil::DebugReport* rep, hipStream_t s) {
+  hipError_t e = qil::launch_check_cu(a.cu_seqlens, a.context_lens, a.batch, a.total_q,
+                                      a.max_seqlen_q, rep, s);
+  if (e == hipSuccess)
+    e = qil::launch_check_tables(a.block_tables, a.bt_stride, a.context_lens, a.batch, a.log2_page,
+                                 a.num_pages, a.max_context_len, rep, s);
+  return e;
+}
+
+// Validate a decode call and fill its launch arguments.  *empty is set when
+// the call has nothing to do (batch == 0).
+int prep_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, int32_t block_table_stride,
+                const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t num_pages,
+                int32_t max_context_len, float scale, int32_t dtype, int32_t keys_per_split,
+                void* workspace, size_t workspace_bytes, qil::DecodeArgs& a, bool* empty) {
+  *empty = false;
+  if (batch < 0) return fail(QIL_EINVAL, "batch %d < 0", batch);
+  if (dtype != QIL_F32 && dtype != QIL_BF16) return fail(QIL_EUNSUPPORTED, "dtype %d", dtype);
+  int rc = check_common(num_q_heads, num_kv_heads, head_dim, page_size, num_pages);
+  if (rc) return rc;
+  if (keys_per_split < 0 || keys_per_split % 64 || keys_per_split > kMaxKeysPerSplit)
+    return fail(QIL_EINVAL, "keys_per_split %d must be 0 or a multiple of 64 up to %d",
+                keys_per_split, kMaxKeysPerSplit);
+  if (batch == 0) {
+    *empty = true;
+    return ok();
+  }
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(QIL_EINVAL, "null pointer argument");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(QIL_EINVAL, "out, q and the pools must be 16-byte aligned");
+  if (block_table_stride <= 0) return fail(QIL_EINVAL, "block_table_stride must be positive");
+  if (max_context_len <= 0) return fail(QIL_EINVAL, "max_context_len must be positive");
+  if ((int64_t)max_context_len > (int64_t)block_table_stride * page_size)
+    return fail(QIL_EINVAL, "max_context_len %d exceeds block_table_stride*page_size", max_context_len);
+  if (!(scale == scale)) return fail(QIL_EINVAL, "scale is NaN");
+  const SplitPlan p = plan_splits(batch, num_kv_heads, max_context_len, keys_per_split);
+  if (p.num_splits > kMaxSplits)
+    return fail(QIL_EINVAL, "max_context_len %d needs %d splits (at most %d)", max_context_len,
+                p.num_splits, kMaxSplits);
+  const size_t need = workspace_bytes_for(batch, num_q_heads, p);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(QIL_EWORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (num_kv_heads > 65535 || batch > 65535)
+    return fail(QIL_EINVAL, "batch and num_kv_heads are limited to 65535");
+
+  a = qil::DecodeArgs{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.bt_stride = block_table_stride;
+  a.context_lens = context_lens;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.log2_page = log2_page_size(page_size);
+  a.num_pages = num_pages;
+  a.max_context_len = max_context_len;
+  a.scale = scale;
+  a.keys_per_split = p.keys_per_split;
+  a.num_splits = p.num_splits;
+  a.bf16 = dtype == QIL_BF16;
+  if (p.num_splits > 1) {
+    const size_t parts = (size_t)batch * num_q_heads * p.num_splits;
+    auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+    char* base = static_cast<char*>(workspace);
+    a.ws_o = reinterpret_cast<float*>(base);
+    a.ws_m = reinterpret_cast<float*>(base + up(parts * qil::kHeadDim * 4));
+    a.ws_l = reinterpret_cast<float*>(base + up(parts * qil::kHeadDim * 4) + up(parts * 4));
+  }
+  return QIL_OK;
+}
+
+// Validate a prefill call and fill its launch arguments.  *empty is set when
+// the call has nothing to do.
+int prep_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, int32_t block_table_stride,
+                 const int32_t* cu_seqlens_q, const int32_t* context_lens, int32_t batch,
+                 int32_t total_q, int32_t max_seqlen_q, int32_t max_context_len,
+                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                 int32_t num_pages, float scale, int32_t dtype, qil::PrefillArgs& a, bool* empty) {
+  *empty = false;
+  if (batch < 0 || total_q < 0 || max_seqlen_q < 0)
+    return fail(QIL_EINVAL, "negative batch / total_q / max_seqlen_q");
+  if (dtype != QIL_BF16) return fail(QIL_EUNSUPPORTED, "prefill is built for bf16 only");
+  int rc = check_common(num_q_heads, num_kv_heads, head_dim, page_size, num_pages);
+  if (rc) return rc;
+  if (batch == 0 || total_q == 0 || max_seqlen_q == 0) {
+    *empty = true;
+    return ok();
+  }
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !cu_seqlens_q || !context_lens)
+    return fail(QIL_EINVAL, "null pointer argument");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(QIL_EINVAL, "out, q and the pools must be 16-byte aligned");
+  if (block_table_stride <= 0) return fail(QIL_EINVAL, "block_table_stride must be positive");
+  if (max_seqlen_q > total_q) return fail(QIL_EINVAL, "max_seqlen_q exceeds total_q");
+  if (max_context_len < max_seqlen_q)
+    return fail(QIL_EINVAL, "max_context_len %d below max_seqlen_q %d", max_context_len,
+                max_seqlen_q);
+  if ((int64_t)max_context_len > (int64_t)block_table_stride * page_size)
+    return fail(QIL_EINVAL, "max_context_len %d exceeds block_table_stride*page_size", max_context_len);
+  if (!(scale == scale)) return fail(QIL_EINVAL, "scale is NaN");
+  if (num_kv_heads > 65535 || batch > 65535)
+    return fail(QIL_EINVAL, "batch and num_kv_heads are limited to 65535");
+
+  a = qil::PrefillArgs{out, q, k_cache, v_cache, block_tables, block_table_stride, cu_seqlens_q,
+                       context_lens, batch, total_q, max_seqlen_q, max_context_len, num_q_heads,
+                       num_kv_heads, log2_page_size(page_size), num_pages, scale};
+  return QIL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -297,66 +419,16 @@ int qil_paged_decode(void* out, const void* q, const void* k_cache, const void* 
                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t num_pages,
                      int32_t max_context_len, float scale, int32_t dtype, int32_t keys_per_split,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  if (batch < 0) return fail(QIL_EINVAL, "batch %d < 0", batch);
-  if (dtype != QIL_F32 && dtype != QIL_BF16) return fail(QIL_EUNSUPPORTED, "dtype %d", dtype);
-  int rc = check_common(num_q_heads, num_kv_heads, head_dim, page_size, num_pages);
-  if (rc) return rc;
-  if (keys_per_split < 0 || keys_per_split % 64 || keys_per_split > kMaxKeysPerSplit)
-    return fail(QIL_EINVAL, "keys_per_split %d must be 0 or a multiple of 64 up to %d",
-                keys_per_split, kMaxKeysPerSplit);
-  if (batch == 0) return ok();
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
-    return fail(QIL_EINVAL, "null pointer argument");
-  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
-    return fail(QIL_EINVAL, "out, q and the pools must be 16-byte aligned");
-  if (block_table_stride <= 0) return fail(QIL_EINVAL, "block_table_stride must be positive");
-  if (max_context_len <= 0) return fail(QIL_EINVAL, "max_context_len must be positive");
-  if ((int64_t)max_context_len > (int64_t)block_table_stride * page_size)
-    return fail(QIL_EINVAL, "max_context_len %d exceeds block_table_stride*page_size", max_context_len);
-  if (!(scale == scale)) return fail(QIL_EINVAL, "scale is NaN");
-  const SplitPlan p = plan_splits(batch, num_kv_heads, max_context_len, keys_per_split);
-  if (p.num_splits > kMaxSplits)
-    return fail(QIL_EINVAL, "max_context_len %d needs %d splits (at most %d)", max_context_len,
-                p.num_splits, kMaxSplits);
-  const size_t need = workspace_bytes_for(batch, num_q_heads, p);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
-    return fail(QIL_EWORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need,
-                workspace ? workspace_bytes : (size_t)0);
-  if (num_kv_heads > 65535 || batch > 65535)
-    return fail(QIL_EINVAL, "batch and num_kv_heads are limited to 65535");
-
-  qil::DecodeArgs a{};
-  a.out = out;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_tables = block_tables;
-  a.bt_stride = block_table_stride;
-  a.context_lens = context_lens;
-  a.batch = batch;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.log2_page = log2_page_size(page_size);
-  a.num_pages = num_pages;
-  a.max_context_len = max_context_len;
-  a.scale = scale;
-  a.keys_per_split = p.keys_per_split;
-  a.num_splits = p.num_splits;
-  a.bf16 = dtype == QIL_BF16;
-  if (p.num_splits > 1) {
-    const size_t parts = (size_t)batch * num_q_heads * p.num_splits;
-    auto up = [](size_t b) { return (b + 255) / 256 * 256; };
-    char* base = static_cast<char*>(workspace);
-    a.ws_o = reinterpret_cast<float*>(base);
-    a.ws_m = reinterpret_cast<float*>(base + up(parts * qil::kHeadDim * 4));
-    a.ws_l = reinterpret_cast<float*>(base + up(parts * qil::kHeadDim * 4) + up(parts * 4));
-  }
+  qil::DecodeArgs a;
+  bool empty = false;
+  int rc = prep_decode(out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens,
+                       batch, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                       max_context_len, scale, dtype, keys_per_split, workspace, workspace_bytes,
+                       a, &empty);
+  if (rc || empty) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (debug_on()) {
-    rc = run_checks(s, [&](qil::DebugReport* rep) {
-      return qil::launch_check_tables(block_tables, block_table_stride, context_lens, batch,
-                                      a.log2_page, num_pages, max_context_len, rep, s);
-    });
+    rc = run_checks(s, [&](qil::DebugReport* rep) { return check_decode_metadata(a, rep, s); });
     if (rc) return rc;
   }
   hipError_t e = qil::launch_decode(a, s);
@@ -371,44 +443,70 @@ int qil_paged_prefill(void* out, const void* q, const void* k_cache, const void*
                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                       int32_t page_size, int32_t num_pages, float scale, int32_t dtype,
                       void* stream) {
-  if (batch < 0 || total_q < 0 || max_seqlen_q < 0)
-    return fail(QIL_EINVAL, "negative batch / total_q / max_seqlen_q");
-  if (dtype != QIL_BF16) return fail(QIL_EUNSUPPORTED, "prefill is built for bf16 only");
-  int rc = check_common(num_q_heads, num_kv_heads, head_dim, page_size, num_pages);
-  if (rc) return rc;
-  if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return ok();
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !cu_seqlens_q || !context_lens)
-    return fail(QIL_EINVAL, "null pointer argument");
-  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
-    return fail(QIL_EINVAL, "out, q and the pools must be 16-byte aligned");
-  if (block_table_stride <= 0) return fail(QIL_EINVAL, "block_table_stride must be positive");
-  if (max_seqlen_q > total_q) return fail(QIL_EINVAL, "max_seqlen_q exceeds total_q");
-  if (max_context_len < max_seqlen_q)
-    return fail(QIL_EINVAL, "max_context_len %d below max_seqlen_q %d", max_context_len,
-                max_seqlen_q);
-  if ((int64_t)max_context_len > (int64_t)block_table_stride * page_size)
-    return fail(QIL_EINVAL, "max_context_len %d exceeds block_table_stride*page_size", max_context_len);
-  if (!(scale == scale)) return fail(QIL_EINVAL, "scale is NaN");
-  if (num_kv_heads > 65535 || batch > 65535)
-    return fail(QIL_EINVAL, "batch and num_kv_heads are limited to 65535");
-
-  qil::PrefillArgs a{out, q, k_cache, v_cache, block_tables, block_table_stride, cu_seqlens_q,
-                     context_lens, batch, total_q, max_seqlen_q, max_context_len, num_q_heads,
-                     num_kv_heads, log2_page_size(page_size), num_pages, scale};
+  qil::PrefillArgs a;
+  bool empty = false;
+  int rc = prep_prefill(out, q, k_cache, v_cache, block_tables, block_table_stride, cu_seqlens_q,
+                        context_lens, batch, total_q, max_seqlen_q, max_context_len, num_q_heads,
+                        num_kv_heads, head_dim, page_size, num_pages, scale, dtype, a, &empty);
+  if (rc || empty) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (debug_on()) {
-    rc = run_checks(s, [&](qil::DebugReport* rep) {
-      hipError_t e = qil::launch_check_cu(cu_seqlens_q, context_lens, batch, total_q,
-                                          max_seqlen_q, rep, s);
-      if (e == hipSuccess)
-        e = qil::launch_check_tables(block_tables, block_table_stride, context_lens, batch,
-                                     a.log2_page, num_pages, max_context_len, rep, s);
-      return e;
-    });
+    rc = run_checks(s, [&](qil::DebugReport* rep) { return check_prefill_metadata(a, rep, s); });
     if (rc) return rc;
   }
   hipError_t e = qil::launch_prefill(a, s);
   if (e != hipSuccess) return fail(QIL_EHIP, "prefill launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int qil_paged_attention_mixed(const qil_decode_batch* decode, const qil_prefill_batch* prefill,
+                              const void* k_cache, const void* v_cache, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                              int32_t num_pages, float scale, int32_t dtype, void* stream) {
+  if (dtype != QIL_BF16) return fail(QIL_EUNSUPPORTED, "the mixed launch is built for bf16 only");
+  qil::DecodeArgs da{};
+  qil::PrefillArgs pa{};
+  bool dec_empty = true, pre_empty = true;
+  int rc;
+  if (decode) {
+    rc = prep_decode(decode->out, decode->q, k_cache, v_cache, decode->block_tables,
+                     decode->block_table_stride, decode->context_lens, decode->batch, num_q_heads,
+                     num_kv_heads, head_dim, page_size, num_pages, decode->max_context_len, scale,
+                     dtype, decode->keys_per_split, decode->workspace, decode->workspace_bytes, da,
+                     &dec_empty);
+    if (rc) return rc;
+  }
+  if (prefill) {
+    rc = prep_prefill(prefill->out, prefill->q, k_cache, v_cache, prefill->block_tables,
+                      prefill->block_table_stride, prefill->cu_seqlens_q, prefill->context_lens,
+                      prefill->batch, prefill->total_q, prefill->max_seqlen_q,
+                      prefill->max_context_len, num_q_heads, num_kv_heads, head_dim, page_size,
+                      num_pages, scale, dtype, pa, &pre_empty);
+    if (rc) return rc;
+  }
+  if (dec_empty && pre_empty) return ok();
+  if (dec_empty) {
+    da = qil::DecodeArgs{};
+    da.num_kv_heads = num_kv_heads;
+    da.num_q_heads = num_q_heads;
+    da.num_splits = 1;
+  }
+  if (pre_empty) {
+    pa = qil::PrefillArgs{};
+    pa.num_kv_heads = num_kv_heads;
+    pa.num_q_heads = num_q_heads;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_on()) {
+    rc = run_checks(s, [&](qil::DebugReport* rep) {
+      hipError_t e = dec_empty ? hipSuccess : check_decode_metadata(da, rep, s);
+      if (e == hipSuccess && !pre_empty) e = check_prefill_metadata(pa, rep, s);
+      return e;
+    });
+    if (rc) return rc;
+  }
+  hipError_t e = qil::launch_mixed(pa, da, s);
+  if (e != hipSuccess) return fail(QIL_EHIP, "mixed launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -1,0 +1,369 @@
+// Chunked varlen causal prefill over the paged cache, on bf16 matrix cores:
+// the device code, included by prefill.hip and mixed.hip.
+//
+// What is computed follows the "nano-vLLM learning note" Attention.forward
+// prefill branch (with a cached prefix the keys come from the cache through
+// the block tables) and prepare_prefill block (the new tokens of a request
+// sit at positions num_cached .. num_cached + n - 1), and the "qwen-engine"
+// README's flat varlen prefill (requests packed by cu_seqlens) and its note
+// that prefill is compute-bound.
+//
+// One workgroup (8 wavefronts, two per SIMD) owns 256 query rows of one
+// request and one KV head: 256/G consecutive new tokens times the G query
+// heads that share the KV head (GQA packing), so each K/V tile fetched from
+// HBM/L2 serves 256 rows.  Each wavefront owns 32 rows.  The workgroup walks
+// key tiles of 64 keys up to its last visible key.
+//
+//   * Tiles go from memory straight into LDS (global_load_lds, 16 bytes per
+//     lane, no staging registers): K and V rows land row-major with the
+//     16-byte chunks XOR-swizzled per row.  LDS is double-buffered: a tile's
+//     loads are in flight while the previous tile is computed.  Each
+//     wavefront keeps the page ids of its rows, one tile per lane, in a
+//     register loaded once per 64 tiles.
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys on the M side, query
+//     rows on the N side), so that each lane owns one query row and the row
+//     statistics of the online softmax stay per lane.
+//   * The PV product O^T = V^T P^T reads V^T operands with
+//     ds_read_b64_tr_b16, which transposes 4x16 blocks of row-major V on the
+//     way out of LDS; P comes straight from the S^T accumulator registers,
+//     rounded to bf16.
+//   * Online softmax in base 2 with a lazy reference maximum: the output is
+//     rescaled only when a row maximum grows by more than 2^8, so the weights
+//     exp2(s - m_ref) stay below 256 and most tiles skip the rescale.  The
+//     check runs once per 64-key tile, on the maximum of the whole tile and
+//     before any weight of the tile is formed, so every weight added to O
+//     and to the row sum is relative to the same reference.  The row sum
+//     adds the same rounded weights that feed the PV product.
+//   * Causal masking only on the diagonal band of tiles.
+//   * Each 64-key tile runs as two 32-key halves: the first half's row
+//     maximum sits next to the second half's QK^T matrix work, and the first
+//     half's PV product next to the second half's exponentials.
+// Block ids are laid out KV-head fastest, so with 8 KV heads all tiles of one
+// KV head land on one XCD (workgroups are dealt to the 8 XCDs round robin)
+// and its K/V stay in that XCD's L2.  Query tiles are issued last-first: the
+// tiles with the most keys start earliest.
+#pragma once
+#include <type_traits>
+
+#include "device_common.h"
+#include "qil_internal.h"
+
+namespace qil {
+namespace {
+
+constexpr int kBN = 64;        // keys per tile
+constexpr float kLazyRescale = 8.0f;  // log2 of the largest weight allowed before rescaling
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Row (M index) of accumulator register v held by lanes of half hf, for the
+// 32x32 MFMA output: rows 8*(v/4) + 4*hf + v%4, column = lane % 32.
+__device__ __forceinline__ int acc_row(int v, int hf) { return 8 * (v >> 2) + 4 * hf + (v & 3); }
+
+// Physical 16-byte chunk of logical chunk c in row `row` of a K tile and of a
+// V tile (256-byte rows, 16 chunks).  K: XOR with row mod 16, so the 16 rows
+// read by a quarter wavefront hit 16 different chunk positions.  V: XOR with
+// 4 * (row mod 4), so the 8 rows of a transposing read fall into four
+// different 64-byte bank groups.
+__device__ __forceinline__ int k_chunk(int row, int c) { return c ^ (row & 15); }
+__device__ __forceinline__ int v_chunk(int row, int c) { return c ^ ((row & 3) << 2); }
+
+// Maximum / sum over the two halves of a wavefront (lanes l and l ^ 32),
+// with v_permlane32_swap instead of an LDS round trip.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+constexpr int kWaves = 8;               // wavefronts per workgroup, 32 query rows each
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsWG = 32 * kWaves;    // query rows per workgroup
+constexpr int kRowsPerWave = kBN / kWaves;  // tile rows each wavefront loads
+
+// LDS of one workgroup: [slot][K | V][64 rows x 256 bytes].
+typedef char PrefillLds[2][2][kBN * 256];
+
+// One query tile: KV head g, request r, tile index z counted from the last
+// tile (z = 0 is the tile with the most keys).  Every thread of the
+// kThreads-thread workgroup calls it; `smem` is the workgroup's LDS.
+template <int G>
+__device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int n_qtiles, int g, int r,
+                                             int z, PrefillLds& smem) {
+  constexpr int TQ = kRowsWG / G;  // tokens per workgroup
+  const int tile = n_qtiles - 1 - z;
+  const int q0 = a.cu_seqlens[r];
+  // rows of this request, kept inside [0, total_q)
+  const int n = min(a.cu_seqlens[r + 1], a.total_q) - max(q0, 0);
+  const int t0 = tile * TQ;
+  if (q0 < 0 || t0 >= n) return;
+  const int L = min(a.context_lens[r], a.max_context_len);
+  const int prefix = L - n;
+  const int tvalid = min(TQ, n - t0);
+  const int kmax = prefix + t0 + tvalid;  // keys [0, kmax) are visible to some row
+  const int ntiles = kmax > 0 ? (kmax + kBN - 1) / kBN : 0;
+  const int pos_min = prefix + t0;
+
+  const int tid = threadIdx.x;
+  const int w = wave_uniform(tid >> 6);
+  const int lane = tid & 63;
+  const int lq = lane & 31;
+  const int hf = lane >> 5;
+  const int Hq = a.num_q_heads;
+
+  // This lane's query row.
+  const int rho = 32 * w + lq;
+  const int tok = rho / G;
+  const int hh = rho % G;
+  const bool row_valid = tok < tvalid;
+  const int my_pos = prefix + t0 + min(tok, tvalid - 1);
+
+  bf16x8_t qreg[8];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                           ((int64_t)(q0 + t0 + tok) * Hq + g * G + hh) * kHeadDim;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      uint4 x = row_valid ? *reinterpret_cast<const uint4*>(qrow + 16 * t + 8 * hf)
+                          : make_uint4(0, 0, 0, 0);
+      qreg[t] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  }
+
+
+  // Rows past the context are never loaded; what they hold stands in for
+  // them (their scores are masked, so their weight is exactly 0) and only has
+  // to be finite: start from zeros.
+  {
+    uint4* zf = reinterpret_cast<uint4*>(&smem[0][0][0]);
+    for (int i = tid; i < (int)(sizeof(PrefillLds) / 16); i += kThreads) zf[i] = make_uint4(0, 0, 0, 0);
+  }
+
+  // Loader role.  Wavefront w fills rows 8w .. 8w+7 of the K and V tiles,
+  // 4 rows (1 KB) per instruction: lane l lands at byte 16 l of that KB,
+  // i.e. row 4m + l/16, physical chunk l%16, so it fetches the logical chunk
+  // that belongs there.  Eight consecutive keys always share a page.
+  const int32_t* bt_row = a.block_tables + (int64_t)r * a.bt_stride;
+  const char* kpool = static_cast<const char*>(a.k_cache);
+  const char* vpool = static_cast<const char*>(a.v_cache);
+  const int P = 1 << a.log2_page;
+  const int lrow = lane >> 4;   // row within a 4-row instruction
+  const int lpc = lane & 15;    // physical chunk this lane fills
+
+  // Lane i holds the page id of this wavefront's rows in tile base + i.
+  int page_lane = -1;
+  auto fetch_pages = [&](int base) __attribute__((always_inline)) {
+    const int key = (base + lane) * kBN + kRowsPerWave * w;
+    page_lane = key < L ? bt_row[key >> a.log2_page] : -1;
+  };
+
+  auto issue_tile = [&](int kt, int buf) __attribute__((always_inline)) {
+    const int page = __builtin_amdgcn_readlane(page_lane, kt & 63);
+    if ((unsigned)page >= (unsigned)a.num_pages) return;  // absent page (uniform)
+#pragma unroll
+    for (int m2 = 0; m2 < kRowsPerWave / 4; ++m2) {
+      const int row = kRowsPerWave * w + 4 * m2 + lrow;  // tile row this lane fills
+      const int key = kt * kBN + row;
+      const int64_t grow = (((int64_t)page * a.num_kv_heads + g) << a.log2_page) + (key & (P - 1));
+      lds_char* kdst = (lds_char*)&smem[buf][0][0] + (kRowsPerWave * w + 4 * m2) * 256;
+      lds_char* vdst = (lds_char*)&smem[buf][1][0] + (kRowsPerWave * w + 4 * m2) * 256;
+      if (key < L) {
+        __builtin_amdgcn_global_load_lds(kpool + grow * 256 + 16 * k_chunk(row, lpc), kdst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vpool + grow * 256 + 16 * v_chunk(row, lpc), vdst, 16, 0, 0);
+      }
+    }
+  };
+
+  // Per-lane LDS offsets of the matrix operands.
+  //  K operand (A of S^T, ds_read_b128): row 32b + lq, logical chunk 2t + hf.
+  const int kx = lq & 15;
+  //  V^T operand (A of O^T) by transposing reads: in each 16-lane group
+  //  (q = lane/16) lane src = j + 4k supplies the 8-byte address of V row
+  //  16s + 8i + 4(q/2) + k, dims 32db + 16(q%2) + 4j .. +3; the hardware hands
+  //  lane o of the group the 4 keys at dim 32db + 16(q%2) + o.  Two reads
+  //  (i = 0, 1) give the 8 keys 16s + 8(e/4) + 4hf + e%4 that the accumulator
+  //  layout of P puts in element e of this lane's B operand.
+  const int q16 = lane >> 4;
+  const int src = lane & 15;
+  const int vj = src & 3, vk = src >> 2;
+  int vofs[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int row = 4 * (q16 >> 1) + vk;  // + 16s + 8i, which keeps row & 3
+    const int c = 4 * db + 2 * (q16 & 1) + (vj >> 1);
+    vofs[db] = row * 256 + 16 * v_chunk(row, c) + 8 * (vj & 1);
+  }
+
+  f32x16_t oacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[i][v] = 0.f;
+  float mref = -1.0e30f;  // base-2 domain
+  float lrun = 0.f;
+  const float qs = a.scale * kLog2e;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const f32x16_t zero16 = {};
+
+  // Operand fetches are separate from the matrix instructions that use them,
+  // so a whole half-tile of LDS reads is in flight before its first MFMA.
+  auto load_k = [&](int buf, int b, bf16x8_t (&kop)[8]) __attribute__((always_inline)) {
+    const char* krow = &smem[buf][0][0] + (32 * b + lq) * 256;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      kop[t] = *reinterpret_cast<const bf16x8_t*>(krow + 16 * ((2 * t + hf) ^ kx));
+  };
+  auto qk = [&](const bf16x8_t (&kop)[8]) __attribute__((always_inline)) -> f32x16_t {
+    f32x16_t acc = zero16;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[t], qreg[t], acc, 0, 0, 0);
+    return acc;
+  };
+  auto load_v = [&](int buf, int b, bf16x8_t (&vop)[4][2]) __attribute__((always_inline)) {
+    const lds_char* vbase = (const lds_char*)&smem[buf][1][0];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int s = 2 * b + s2;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(vbase + vofs[db] + (16 * s) * 256));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(vbase + vofs[db] + (16 * s + 8) * 256));
+        const i16x8_t v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        vop[db][s2] = __builtin_bit_cast(bf16x8_t, v8);
+      }
+    }
+  };
+  auto pv = [&](const bf16x8_t (&vop)[4][2], const bf16x8_t (&pb)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][s2], pb[s2], oacc[db], 0, 0, 0);
+  };
+
+  // Masked row maximum (raw scores) of a half.
+  auto half_max = [&](auto mask_tag, f32x16_t& s, int kbase, float& mx) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      if (MASK && kbase + acc_row(v, hf) > my_pos) s[v] = -INFINITY;
+      mx = fmaxf(mx, s[v]);
+    }
+  };
+  // The lazy rescale, once per tile before any weight of the tile is formed
+  // (a uniform branch, rarely taken).
+  auto rescale = [&](float mx) __attribute__((always_inline)) {
+    mx = max_halves(mx) * qs;
+    if (__ballot(mx > mref + kLazyRescale) != 0) {
+      asm volatile("" ::: "memory");  // keep the rare rescale a real branch
+      const float mnew = fmaxf(mref, mx);
+      const float corr = fast_exp2(mref - mnew);
+      mref = mnew;
+      lrun *= corr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[i][v] *= corr;
+    }
+  };
+
+  // Weights of a half as two bf16 B operands; the row sum takes them too.
+  auto exp_half = [&](const f32x16_t& s, bf16x8_t (&pb)[2]) __attribute__((always_inline)) {
+    const float neg = -mref;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      uint32_t pk[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = fast_exp2(fmaf(s[8 * s2 + 2 * i], qs, neg));
+        const float p1 = fast_exp2(fmaf(s[8 * s2 + 2 * i + 1], qs, neg));
+        pk[i] = cvt_pk_bf16(p0, p1);
+        lrun = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[i]), ones, lrun, false);
+      }
+      const uint4 u = {pk[0], pk[1], pk[2], pk[3]};
+      pb[s2] = __builtin_bit_cast(bf16x8_t, u);
+    }
+  };
+
+  // One tile as two 32-key halves.
+  auto compute = [&](auto mask_tag, int buf, int kt) __attribute__((always_inline)) {
+    const int kbase = kt * kBN;
+    bf16x8_t kop[8];
+    bf16x8_t vop[4][2];
+    bf16x8_t p0[2], p1[2];
+    load_k(buf, 0, kop);
+    f32x16_t s0 = qk(kop);
+    // all eight operand reads first, then the eight MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    load_k(buf, 1, kop);
+    float mx = -INFINITY;
+    half_max(mask_tag, s0, kbase, mx);
+    f32x16_t s1 = qk(kop);
+    half_max(mask_tag, s1, kbase + 32, mx);
+    rescale(mx);
+    load_v(buf, 0, vop);
+    exp_half(s0, p0);
+    pv(vop, p0);
+    load_v(buf, 1, vop);
+    exp_half(s1, p1);
+    pv(vop, p1);
+  };
+
+  // Tiles [0, nfree) lie wholly at or before the first token's position and
+  // need no mask; the rest (the diagonal band) are masked.
+  const int nfree = min(ntiles, (pos_min + 1) / kBN);
+  auto tile_step = [&](auto mask_tag, int kt) __attribute__((always_inline)) {
+    const int buf = kt & 1;
+    if (kt + 1 < ntiles) {
+      if (((kt + 1) & 63) == 0) fetch_pages(kt + 1);
+      issue_tile(kt + 1, buf ^ 1);
+    }
+    compute(mask_tag, buf, kt);
+    __builtin_amdgcn_s_waitcnt(0);  // this wavefront's loads of the next tile have landed
+    __syncthreads();
+  };
+  if (ntiles > 0) {
+    fetch_pages(0);
+    __syncthreads();  // the zero fill is complete before any load lands
+    issue_tile(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = 0; kt < nfree; ++kt) tile_step(std::false_type{}, kt);
+    for (int kt = nfree; kt < ntiles; ++kt) tile_step(std::true_type{}, kt);
+  }
+
+  const float ltot = sum_halves(lrun);
+  if (!row_valid) return;
+  const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+  uint16_t* orow =
+      static_cast<uint16_t*>(a.out) + ((int64_t)(q0 + t0 + tok) * Hq + g * G + hh) * kHeadDim;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * db + 8 * q4 + 4 * hf;
+      uint2 st;
+      st.x = pack_bf16x2(oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv);
+      st.y = pack_bf16x2(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv);
+      *reinterpret_cast<uint2*>(orow + d0) = st;
+    }
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int n_qtiles) {
+  __shared__ __attribute__((aligned(1024))) PrefillLds smem;
+  prefill_tile<G>(a, n_qtiles, blockIdx.x, blockIdx.y, blockIdx.z, smem);
+}
+
+}  // namespace
+}  // namespace qil

@@ -69,6 +69,8 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// the split merge alone (num_splits > 1), for launches that ran the splits
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s);
 
 // ---- prefill ---------------------------------------------------------------
 struct PrefillArgs {
@@ -92,6 +94,10 @@ struct PrefillArgs {
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+
+// ---- single-launch mixed batch (bf16): prefill tiles and decode splits ----
+// in one grid, then the decode merge when the decode part has several splits
+hipError_t launch_mixed(const PrefillArgs& pa, const DecodeArgs& da, hipStream_t s);
 
 }  // namespace qil
 

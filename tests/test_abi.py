@@ -131,6 +131,16 @@ def test_rope_table_validation(lib):
     assert lib.qil_rope_cos_sin(FAKE, 10, 128, 0.5, None) == EINVAL
 
 
+def test_mixed_validation(lib):
+    args = (FAKE, FAKE, 16, 8, 128, 16, 100, 0.088)
+    assert lib.qil_paged_attention_mixed(None, None, *args, 1, None) == 0      # nothing to do
+    assert lib.qil_paged_attention_mixed(None, None, *args, 0, None) == EUNSUP  # bf16 only
+    d = qil._DecodeBatchC(FAKE, FAKE, FAKE, 128, FAKE, 2, 2048, 0, None, 0)
+    assert lib.qil_paged_attention_mixed(ctypes.pointer(d), None, *args, 1, None) == EWS
+    p = qil._PrefillBatchC(FAKE, FAKE, FAKE, 200, FAKE, FAKE, 8, 8000, 9000, 2560)
+    assert lib.qil_paged_attention_mixed(None, ctypes.pointer(p), *args, 1, None) == EINVAL
+
+
 def test_debug_switch(lib):
     was = lib.qil_debug_enabled()
     lib.qil_set_debug(1)
