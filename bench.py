@@ -579,9 +579,24 @@ def cpu_baseline(seconds):
                                    f"first), {pflops / 1e9:.1f} causal GFLOP in {pbusy:.1f} s"})
 
 
-def traffic_for(kernel_file, launches_bytes_key):
+KERNEL_SOURCES = {
+    "decode-b256": ("decode.hip", "decode_body.h"),
+    "prefill-varlen": ("prefill.hip", "prefill_body.h"),
+}
+
+
+def sources_sha256(files):
+    """SHA-256 over the kernel's source files, in order."""
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "paged_kv_attention_16_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_for(launches_bytes_key):
     """HBM bytes per launch from committed counter runs, only while the
-    kernel source is unchanged since the counters were taken."""
+    kernel's sources are unchanged since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -590,9 +605,7 @@ def traffic_for(kernel_file, launches_bytes_key):
     entry = table.get(launches_bytes_key)
     if not entry:
         return None
-    src = os.path.join(ROOT, "paged_kv_attention_16_amd", "csrc", kernel_file)
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if entry.get("source_sha256") != sha:
+    if entry.get("source_sha256") != sources_sha256(KERNEL_SOURCES[launches_bytes_key]):
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -640,7 +653,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_for("decode.hip", "decode-b256"),
+            "traffic": traffic_for("decode-b256"),
             "algorithmic_bytes_per_launch": int(dec["dec_bytes"]),
             "launch_us_mean": round(dec["dec_ms"] * 1e3, 2),
             "launch_timing": "mean step time with no marker between the kernels, minus the "
@@ -671,7 +684,7 @@ def main():
             "event_bracket_us_mean": round(p["pre_bracket_ms"] * 1e3, 2),
             "event_bracket_us_median": round(p["pre_bracket_ms_median"] * 1e3, 2),
             "step_us_mean": round(p["step_ms"] * 1e3, 2),
-            "traffic": traffic_for("prefill.hip", "prefill-varlen"),
+            "traffic": traffic_for("prefill-varlen"),
             "measured_ceiling": res["ceilings"]["mfma_bf16_TFLOP_s"],
             "frac_of_measured": round(tf / res["ceilings"]["mfma_bf16_TFLOP_s"], 4),
         }
