@@ -27,7 +27,8 @@
  *    All argument checks happen before any HIP call, so they run on a host
  *    without a GPU.  No exception crosses the ABI and nothing aborts.
  *  - head_dim must be 128.  page_size must be 16, 32, 64, 128 or 256.
- *    num_q_heads must be num_kv_heads * G with G in {1, 2, 4, 8}.
+ *    num_q_heads must be num_kv_heads * G with G in {1, 2, 4, 5, 8, 16}
+ *    (G <= 8 for fp32 decode).
  *  - dtype: QIL_F32 (IEEE binary32) or QIL_BF16 (bfloat16).  Outputs have the
  *    input dtype; accumulation is fp32.  Pointers must be 16-byte aligned.
  *  - Device-resident metadata (slots, page ids, lengths) is a precondition,

@@ -120,7 +120,8 @@ int log2_page_size(int32_t page_size) {
 bool supported_group(int32_t hq, int32_t hkv) {
   if (hkv <= 0 || hq <= 0 || hq % hkv != 0) return false;
   const int g = hq / hkv;
-  return g == 1 || g == 2 || g == 4 || g == 8;
+  // 1 (MHA), 2 (Qwen3-0.6B / 1.7B), 4 (4B, 8B, 30B-A3B), 5 (14B), 8 (32B), 16 (235B-A22B)
+  return g == 1 || g == 2 || g == 4 || g == 5 || g == 8 || g == 16;
 }
 
 int check_common(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
@@ -131,7 +132,7 @@ int check_common(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, in
     return fail(QIL_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
                 num_kv_heads);
   if (!supported_group(num_q_heads, num_kv_heads))
-    return fail(QIL_EUNSUPPORTED, "GQA group size %d not built (1, 2, 4, 8)",
+    return fail(QIL_EUNSUPPORTED, "GQA group size %d not built (1, 2, 4, 5, 8, 16)",
                 num_q_heads / num_kv_heads);
   if (head_dim != qil::kHeadDim)
     return fail(QIL_EUNSUPPORTED, "head_dim %d not built (128)", head_dim);
@@ -213,6 +214,8 @@ int prep_decode(void* out, const void* q, const void* k_cache, const void* v_cac
   if (keys_per_split < 0 || keys_per_split % 64 || keys_per_split > kMaxKeysPerSplit)
     return fail(QIL_EINVAL, "keys_per_split %d must be 0 or a multiple of 64 up to %d",
                 keys_per_split, kMaxKeysPerSplit);
+  if (dtype == QIL_F32 && num_q_heads / num_kv_heads > 8)
+    return fail(QIL_EUNSUPPORTED, "fp32 decode is built for GQA group sizes up to 8");
   if (batch == 0) {
     *empty = true;
     return ok();

@@ -333,7 +333,11 @@ hipError_t launch_dtype(const DecodeArgs& a, hipStream_t s) {
     case 1: return launch_g<1, BF16>(a, s);
     case 2: return launch_g<2, BF16>(a, s);
     case 4: return launch_g<4, BF16>(a, s);
+    case 5: return launch_g<5, BF16>(a, s);
     case 8: return launch_g<8, BF16>(a, s);
+    case 16:
+      if constexpr (BF16) return launch_g<16, true>(a, s);
+      return hipErrorInvalidValue;  // fp32 is built up to G = 8 (validated before)
     default: return hipErrorInvalidValue;
   }
 }

@@ -79,7 +79,9 @@ hipError_t launch_mixed(const PrefillArgs& pa, const DecodeArgs& da, hipStream_t
     case 1: return launch_g<1>(pa, da, s);
     case 2: return launch_g<2>(pa, da, s);
     case 4: return launch_g<4>(pa, da, s);
+    case 5: return launch_g<5>(pa, da, s);
     case 8: return launch_g<8>(pa, da, s);
+    case 16: return launch_g<16>(pa, da, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -22,7 +22,9 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     case 1: return launch_g<1>(a, s);
     case 2: return launch_g<2>(a, s);
     case 4: return launch_g<4>(a, s);
+    case 5: return launch_g<5>(a, s);
     case 8: return launch_g<8>(a, s);
+    case 16: return launch_g<16>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -91,6 +91,8 @@ def test_decode_validation(lib):
     assert dec(lib, ws=FAKE, wsb=need - 1) == EWS
     assert dec(lib, hq=12) == EINVAL
     assert dec(lib, hq=24) == EUNSUP                # G = 3
+    assert dec(lib, hq=48) == EUNSUP                # G = 6
+    assert dec(lib, hq=128, dtype=0) == EUNSUP      # fp32 is built up to G = 8
     assert dec(lib, d=256) == EUNSUP
     assert dec(lib, page=1) == EUNSUP
     assert dec(lib, S=100) == EINVAL                # not a multiple of 64

@@ -115,7 +115,8 @@ def test_single_key_returns_v(qil):
     assert np.array_equal(out, np.repeat(v, 2, axis=1))
 
 
-@pytest.mark.parametrize("hq,hkv,page", [(32, 8, 16), (8, 8, 32), (64, 8, 128), (4, 1, 16)])
+@pytest.mark.parametrize("hq,hkv,page", [(32, 8, 16), (8, 8, 32), (64, 8, 128), (4, 1, 16),
+                                         (40, 8, 16), (64, 4, 64)])
 def test_gqa_shapes(qil, hq, hkv, page):
     w = make_custom([700, 33, 4096, 5, 129], [1] * 5, hq=hq, hkv=hkv, page=page, seed=hq + page,
                     decode=True)

@@ -65,7 +65,7 @@ def test_mixed_step_8b_layer(qil):
     assert H.excess(got, ref, "bf16") <= 0
 
 
-@pytest.mark.parametrize("hq,hkv", [(16, 8), (32, 8), (8, 8), (16, 2)])
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (32, 8), (8, 8), (16, 2), (40, 8), (64, 4)])
 def test_mixed_small_groups(qil, hq, hkv):
     # decode requests (1 new token) and prefill requests in one workload
     ctx = [700, 33, 1, 260, 1500, 90, 64]

@@ -23,7 +23,7 @@ def test_cfg4_full(qil):
     assert H.excess(out, ref, "bf16") <= 0
 
 
-@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (32, 8), (16, 2)])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (32, 8), (16, 2), (40, 8), (64, 4)])
 def test_group_sizes_ragged(qil, hq, hkv):
     # chunk lengths straddle the query tile (128 / G tokens) and key tile (64)
     ctx = [1, 65, 200, 129, 700, 33]
