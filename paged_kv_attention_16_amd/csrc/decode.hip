@@ -69,21 +69,6 @@ __device__ __forceinline__ void unpack_f32(const RowF32& c, float x[8]) {
   x[6] = __uint_as_float(c.b.z); x[7] = __uint_as_float(c.b.w);
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
-}
-
-// Sum over the 16 lanes of a row with DPP: swap neighbours, swap pairs,
-// mirror within 8, mirror within 16.  Every lane ends with the same sum.
-__device__ __forceinline__ float row_sum16(float x) {
-  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
-  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
-  x += dpp_mov<0x141>(x);  // row_half_mirror
-  x += dpp_mov<0x140>(x);  // row_mirror
-  return x;
-}
-
 template <int G>
 __global__ __launch_bounds__(64 * kFW) void decode_f32_kernel(DecodeArgs a) {
   const int split = blockIdx.x;

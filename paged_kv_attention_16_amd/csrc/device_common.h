@@ -43,4 +43,23 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Cross-lane move within a 16-lane row (DPP control CTRL).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
+// Sum over the 16 lanes of a row with DPP: swap neighbours, swap pairs,
+// mirror within 8, mirror within 16.  Every lane ends with the same sum.
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_mov<0x141>(x);  // row_half_mirror
+  x += dpp_mov<0x140>(x);  // row_mirror
+  return x;
+}
+
+// The value of the lane 8 away within a 16-lane row (row_ror:8).
+__device__ __forceinline__ float row_swap8(float x) { return dpp_mov<0x128>(x); }
+
 }  // namespace qil

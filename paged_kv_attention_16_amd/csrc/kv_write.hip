@@ -99,8 +99,7 @@ __global__ __launch_bounds__(256) void kv_write_fused_kernel(KvWriteArgs a, Fuse
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) ss += __shfl_xor(ss, off, 16);
+  ss = row_sum16(ss);  // the 16 lanes of the row
   const float inv_rms = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + f.eps);
 
   const uint4 wraw = *reinterpret_cast<const uint4*>(
@@ -109,9 +108,12 @@ __global__ __launch_bounds__(256) void kv_write_fused_kernel(KvWriteArgs a, Fuse
   float y[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    // bf16(x * r), then bf16(that * w): the two casts of rms_forward
-    y[2 * i] = round_bf16(round_bf16(x[2 * i] * inv_rms) * bf16_lo(ww[i]));
-    y[2 * i + 1] = round_bf16(round_bf16(x[2 * i + 1] * inv_rms) * bf16_hi(ww[i]));
+    // bf16(x * r), then bf16(that * w): the two casts of rms_forward, each a
+    // round-to-nearest-even pair conversion
+    const uint32_t n = cvt_pk_bf16(x[2 * i] * inv_rms, x[2 * i + 1] * inv_rms);
+    const uint32_t m = cvt_pk_bf16(bf16_lo(n) * bf16_lo(ww[i]), bf16_hi(n) * bf16_hi(ww[i]));
+    y[2 * i] = bf16_lo(m);
+    y[2 * i + 1] = bf16_hi(m);
   }
 
   int pos = f.positions[t];
@@ -131,11 +133,11 @@ __global__ __launch_bounds__(256) void kv_write_fused_kernel(KvWriteArgs a, Fuse
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int e = 2 * i + h;
-      const float partner = __shfl_xor(y[e], 8, 16);
+      const float partner = row_swap8(y[e]);
       // first half: y1*c - y2*s ; second half: y2*c + y1*s
       r[h] = first_half ? (y[e] * cv[e] - partner * sv[e]) : (y[e] * cv[e] + partner * sv[e]);
     }
-    o32[i] = pack_bf16x2(r[0], r[1]);
+    o32[i] = cvt_pk_bf16(r[0], r[1]);
   }
   const uint4 outv = {o32[0], o32[1], o32[2], o32[3]};
   if (is_q) {
