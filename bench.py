@@ -176,6 +176,15 @@ def timed_steps(segments, steps, warmup, flush, stream):
                 last_ms=float(step.mean() - mean[:-1].sum()))
 
 
+def flushed_kernel_ms(fn, args, flush, stream):
+    """Mean time of `fn` right after the cache flush, with no event marker in
+    front of it: time of (flush, fn) minus time of (flush)."""
+    if flush is None:
+        return timed_steps([fn], args.steps, args.warmup, None, stream)["step_mean"]
+    return timed_steps([lambda: flush.fill_(1.0), fn], args.steps, args.warmup, None,
+                       stream)["last_ms"]
+
+
 def write_bytes(w, tokens):
     """Algorithmic bytes of a scatter write: read and write both rows."""
     return tokens * w.num_kv_heads * w.head_dim * w.elem_bytes * 2 * 2 + 4 * tokens
@@ -252,12 +261,7 @@ def gpu_legs(args):
         t = timed_steps([write4, prefill], args.steps, args.warmup, flush, stream)
         # the chunk write alone, right after the flush writes (no event marker
         # in front of it): time of (flush, write) minus time of the flush
-        if flush is not None:
-            tw = timed_steps([lambda: flush.fill_(1.0), write4], args.steps, args.warmup, None,
-                             stream)
-            write_ms = tw["last_ms"]
-        else:
-            write_ms = float(t["mean"][0])
+        write_ms = flushed_kernel_ms(write4, args, flush, stream)
         flops = w4.prefill_flops()
         ntok = int(w4.new_lens.sum())
         res["prefill"] = dict(workload=w4, pre_ms=t["last_ms"], pre_bracket_ms=float(t["mean"][1]),
@@ -351,6 +355,7 @@ def gpu_legs(args):
         res["graph"] = graph_leg(args, dev, stream, flush)
     if not args.skip_shared:
         res["shared"] = shared_prefix_leg(args, dev, stream, flush)
+    res["shard"] = shard_leg(args, dev, stream, flush)
     return res
 
 
@@ -436,6 +441,52 @@ def shared_prefix_leg(args, dev, stream, flush):
 
 
 GRAPH_BUCKETS = (1, 2, 4, 8, 16, 32, 64, 128, 256)
+
+
+def shard_leg(args, dev, stream, flush):
+    """Decode at one GPU's share of an 8-way tensor-parallel split by KV head
+    (each GPU holds Hkv/8 = 1 KV head and its G query heads; no exchange is
+    needed inside attention).  Fewer workgroups per call, so the split plan
+    carries the parallelism.  Synthetic N(0,1) bf16 pools, random placement."""
+    import torch
+    import paged_kv_attention_16_amd as qil
+    rng = np.random.default_rng(13)
+    cases = [
+        ("0.6B TP8: B 256, Hq 2 / Hkv 1, page 256, context U[16,1024]+U[0,1024]", 256, 2, 256,
+         rng.integers(16, 1025, 256) + rng.integers(0, 1025, 256)),
+        ("8B TP8: B 64, Hq 4 / Hkv 1, page 16, context U[512,8192]", 64, 4, 16,
+         rng.integers(512, 8193, 64)),
+    ]
+    out = []
+    for label, B, hq, page, ctx in cases:
+        ctx = ctx.astype(np.int32)
+        need = -(-ctx // page)
+        num_pages = int(np.ceil(need.sum() * 1.2))
+        perm = rng.permutation(num_pages).astype(np.int32)
+        bt = np.full((B, int(need.max())), -1, np.int32)
+        at = 0
+        for r, k in enumerate(need.tolist()):
+            bt[r, :k] = perm[at:at + k]
+            at += k
+        kp = torch.empty(num_pages, 1, page, 128, dtype=torch.bfloat16, device=dev).normal_()
+        vp = torch.empty_like(kp).normal_()
+        q = torch.randn(B, hq, 128, device=dev).to(torch.bfloat16)
+        o = torch.empty_like(q)
+        bt_d, ctx_d = torch.from_numpy(bt).to(dev), torch.from_numpy(ctx).to(dev)
+        maxl = int(ctx.max())
+        wsz = qil.paged_decode_workspace_size(B, hq, 1, maxl, page, 0)
+        ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=dev)
+        ms = flushed_kernel_ms(lambda: qil.paged_decode(o, q, kp, vp, bt_d, ctx_d, maxl,
+                                                        0.08838834764831845, workspace=ws,
+                                                        stream=stream), args, flush, stream)
+        nbytes = int(ctx.astype(np.int64).sum()) * 512 + 2 * B * hq * 256
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out.append(dict(workload=label, us=round(ms * 1e3, 2), GB_per_s=round(gbs, 1),
+                        frac=round(gbs / HBM_PEAK_GBS, 4)))
+        print(f"[bench] shard {label}: {ms*1e3:.1f} us, {gbs:.0f} GB/s", flush=True)
+        del kp, vp
+    torch.cuda.empty_cache()
+    return out
 
 
 def measured_ceilings(dev, stream):
@@ -734,6 +785,8 @@ def main():
                         "private copies; prefill: 8 chunks of 512 after it; decode: 64 requests "
                         "with private tails U[1,1024]",
             **res["shared"]}
+    if "shard" in res:
+        line["tp8_shard_decode"] = res["shard"]
     if not args.skip_cpu:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)
