@@ -10,6 +10,7 @@ never imports it.
 Sources (web pages; cited by page title and the code block or section):
   * "nano-vLLM learning note" (floratopia): the ``store_kvcache_kernel``,
     ``RMSNorm.rms_forward``, ``apply_rotary_emb``, ``RotaryEmbedding``,
+    ``QKVParallelLinear``, ``Qwen3Attention.forward``,
     ``ModelRunner.prepare_prefill`` / ``prepare_decode``, ``Context`` and
     ``allocate_kv_cache`` code blocks.
   * "qwen-inference-lab" README (qil): feature list (GQA, Q/K RMSNorm,
@@ -26,10 +27,12 @@ Modules:
                 + scatter write, with the pages' rounding points.
   attention  -- GQA causal softmax attention read through block tables
                 (decode is the one-query-token case of prefill).
+  projection -- the merged QKV linear layer ahead of the fused write
+                ([Q | K | V] columns, bf16 output).
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against closed
 forms, library routines (torch float64 SDPA / rms_norm, numpy complex
 arithmetic) and invariants the pages fix.
 """
 
-from . import bf16, paged, norm_rope, attention  # noqa: F401
+from . import bf16, paged, norm_rope, attention, projection  # noqa: F401

@@ -195,6 +195,20 @@ class Workload:
         b = bf16_from_f32(w)
         return b[0].copy(), b[1].copy()
 
+    def projection_inputs(self, hidden, tokens=None):
+        """Inputs of the merged QKV projection ahead of the fused write, bf16
+        bits: activations x [T][hidden] ~ N(0, 1) (the input RMSNorm leaves
+        rows at unit scale) and the weight [(Hq + 2 Hkv) * D][hidden] ~
+        N(0, 1/hidden), so the projected rows are near unit scale, like the q,
+        k and v the other configs draw directly.  T defaults to every new
+        token of the workload."""
+        rng = _rng(self.cfg, self.layer, 3, hidden)
+        t = int(self.new_lens.sum()) if tokens is None else int(tokens)
+        n = (self.num_q_heads + 2 * self.num_kv_heads) * self.head_dim
+        x = rng.standard_normal((t, hidden), dtype=np.float32)
+        w = rng.standard_normal((n, hidden), dtype=np.float32) * np.float32(1.0 / np.sqrt(hidden))
+        return bf16_from_f32(x), bf16_from_f32(w)
+
     def gather(self, requests=None):
         """All requests' data concatenated in request order:
         (k_cached, v_cached, cached_slots, k_new, v_new, q, new_slots)."""
