@@ -57,6 +57,9 @@ def parse():
                          "(28 in Qwen3-0.6B; 0 skips the leg)")
     ap.add_argument("--skip-shared", action="store_true",
                     help="skip the shared-prefix leg (prefill and decode over a common prefix)")
+    ap.add_argument("--skip-qkv-proj", action="store_true",
+                    help="skip the QKV-projection leg (projection GEMM with the fused write as "
+                         "its epilogue, vs a library GEMM followed by the fused write)")
     ap.add_argument("--calibrate", action="store_true",
                     help="time torch's copy and sum over 1 GiB (reference ceilings and the "
                          "plain copy kernel used to scale HBM byte counters), then exit")
@@ -356,6 +359,8 @@ def gpu_legs(args):
     if not args.skip_shared:
         res["shared"] = shared_prefix_leg(args, dev, stream, flush)
     res["shard"] = shard_leg(args, dev, stream, flush)
+    if not args.skip_qkv_proj:
+        res["qkv_proj"] = qkv_proj_leg(args, dev, stream, flush)
     return res
 
 
@@ -487,6 +492,60 @@ def shard_leg(args, dev, stream, flush):
         del kp, vp
     torch.cuda.empty_cache()
     return out
+
+
+def qkv_proj_leg(args, dev, stream, flush):
+    """The merged QKV projection of the Qwen3-8B-shaped step (2112 new tokens:
+    64 decode + 4 x 512 chunk, hidden 4096, 32 q / 8 KV heads, page 16) with
+    the Q/K RMSNorm + RoPE + scatter write as its epilogue, in one kernel;
+    next to it, the same work as a library GEMM (torch.matmul) followed by
+    the fused qil_kv_write.  Synthetic activations N(0,1) and weights
+    N(0, 1/hidden), bf16."""
+    import torch
+    import paged_kv_attention_16_amd as qil
+    from workloads import make_workload
+    w5 = make_workload(5)
+    hidden = 4096
+    x_bits, w_bits = w5.projection_inputs(hidden)
+    t, n = x_bits.shape[0], w_bits.shape[0]
+    hq, hkv = w5.num_q_heads, w5.num_kv_heads
+    x = torch.from_numpy(x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    wt = torch.from_numpy(w_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    kp = torch.zeros(w5.num_pages, hkv, w5.page_size, 128, dtype=torch.bfloat16, device=dev)
+    vp = torch.zeros_like(kp)
+    qw, kw = (torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+              for a in w5.norm_weights())
+    table = torch.empty(w5.max_position, 128, dtype=torch.float32, device=dev)
+    qil.rope_cos_sin(table, w5.theta, stream=stream)
+    slots = _i32(w5.slot_mapping_new(), dev)
+    pos = _i32(w5.positions_new(), dev)
+    q_out = torch.empty(t, hq, 128, dtype=torch.bfloat16, device=dev)
+    qkv = torch.empty(t, n, dtype=torch.bfloat16, device=dev)
+
+    def fused():
+        qil.qkv_proj_write(x, wt, kp, vp, slots, q_out, hq, qw, kw, pos, table, eps=w5.eps,
+                           stream=stream)
+
+    def gemm():
+        torch.matmul(x, wt.t(), out=qkv)
+
+    fuse = qil.QKNormRope(qkv[:, :hq * 128], q_out, qw, kw, pos, table, eps=w5.eps, num_q_heads=hq)
+
+    def write():
+        qil.kv_write(qkv[:, hq * 128:(hq + hkv) * 128], qkv[:, (hq + hkv) * 128:], kp, vp, slots,
+                     fuse=fuse, stream=stream)
+
+    with torch.cuda.stream(stream):
+        fused_ms = flushed_kernel_ms(fused, args, flush, stream)
+        gemm_ms = flushed_kernel_ms(gemm, args, flush, stream)
+        write_ms = flushed_kernel_ms(write, args, flush, stream)
+    flops = 2 * t * n * hidden
+    tf = flops / (fused_ms * 1e-3) / 1e12
+    print(f"[bench] qkv-proj-8b: one kernel {fused_ms*1e3:.1f} us ({tf:.0f} TFLOP/s); "
+          f"library GEMM {gemm_ms*1e3:.1f} us + fused write {write_ms*1e3:.1f} us", flush=True)
+    del kp, vp
+    torch.cuda.empty_cache()
+    return dict(tokens=t, flops=flops, fused_ms=fused_ms, gemm_ms=gemm_ms, write_ms=write_ms)
 
 
 def measured_ceilings(dev, stream):
@@ -785,6 +844,18 @@ def main():
                         "private copies; prefill: 8 chunks of 512 after it; decode: 64 requests "
                         "with private tails U[1,1024]",
             **res["shared"]}
+    if "qkv_proj" in res:
+        qp = res["qkv_proj"]
+        tf = qp["flops"] / (qp["fused_ms"] * 1e-3) / 1e12
+        line["qkv_proj"] = {
+            "workload": f"qkv-proj-8b: {qp['tokens']} tokens x hidden 4096 -> 32 q + 2 x 8 KV heads "
+                        "(N 6144), Q/K RMSNorm + RoPE + scatter into page-16 pools as the epilogue",
+            "bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            "flops": int(qp["flops"]), "launch_us": round(qp["fused_ms"] * 1e3, 2),
+            "library_gemm_then_fused_write_us": {
+                "gemm": round(qp["gemm_ms"] * 1e3, 2), "fused_write": round(qp["write_ms"] * 1e3, 2),
+                "total": round((qp["gemm_ms"] + qp["write_ms"]) * 1e3, 2)}}
     if "shard" in res:
         line["tp8_shard_decode"] = res["shard"]
     if not args.skip_cpu:

@@ -164,6 +164,44 @@ int qil_rope_cos_sin(float* cos_sin, int32_t max_position, int32_t head_dim, dou
                      void* stream);
 
 /*
+ * qil_qkv_proj_write -- the merged QKV projection with the fused write as its
+ * epilogue ("nano-vLLM learning note": QKVParallelLinear gives one linear
+ * layer whose output columns are all q heads, then all k heads, then all v
+ * heads; Qwen3Attention.forward projects, splits per head, applies q_norm /
+ * k_norm and rotary_emb, and its attention step stores k and v).  bf16 only;
+ * one kernel, matrix cores with fp32 accumulation.
+ *
+ * For every token t and output column n of N = (Hq + 2 Hkv) * head_dim:
+ *     qkv[t][n] = bf16( sum_k x[t][k] * weight[n][k] )      (no bias)
+ * then columns [0, Hq*D) are the q heads, [Hq*D, (Hq+Hkv)*D) the k heads and
+ * the rest the v heads, and each head row goes through exactly what
+ * qil_kv_write does with a qil_qknorm_rope: q and k rows are normalised,
+ * weighted and rotated (the formula above that struct), rotated k rows and
+ * the projected v rows are stored at slot_mapping[t] (-1 = skip), and the
+ * rotated q rows go to q_out.
+ *
+ *   x               bf16, token t's `hidden` values at x + t*x_token_stride
+ *   weight          bf16 nn.Linear layout: row n (N rows) at weight + n*weight_row_stride,
+ *                   `hidden` values each
+ *   hidden          multiple of 64; strides are multiples of 8 elements and >= hidden
+ *   q_out           bf16 [num_tokens][num_q_heads][head_dim]
+ *   qkv_out         NULL, or bf16 [num_tokens][N]: also store the rounded projection
+ *   k_cache/v_cache, slot_mapping, page_size, num_pages: as for qil_kv_write
+ *   q_norm_weight, k_norm_weight, eps, positions, cos_sin, max_position:
+ *                   as in qil_qknorm_rope
+ * Hq + 2 Hkv must be even (workgroups own pairs of heads).  Outputs must not
+ * overlap the inputs.  num_tokens == 0 is a no-op.
+ */
+int qil_qkv_proj_write(const void* x, int64_t x_token_stride, const void* weight,
+                       int64_t weight_row_stride, int32_t hidden, void* q_out, void* qkv_out,
+                       void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                       int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t page_size, int32_t num_pages,
+                       const void* q_norm_weight, const void* k_norm_weight, float eps,
+                       const int32_t* positions, const float* cos_sin, int32_t max_position,
+                       int32_t dtype, void* stream);
+
+/*
  * qil_paged_decode -- one query token per request over its paged context
  * ("nano-vLLM learning note", Attention.forward decode branch and
  * prepare_decode: the token's position is context_len - 1; "qwen-engine"

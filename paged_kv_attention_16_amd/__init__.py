@@ -11,6 +11,8 @@ The functions mirror the C ABI in include/qil.h:
   rope_cos_sin(table, theta)
   paged_decode(out, q, k_cache, v_cache, block_tables, context_lens, ...)
   paged_prefill(out, q, k_cache, v_cache, block_tables, cu_seqlens_q, context_lens, ...)
+  paged_attention_mixed(k_cache, v_cache, scale, decode=..., prefill=...)
+  qkv_proj_write(x, weight, k_cache, v_cache, slot_mapping, q_out, ...)
 Pools are torch tensors shaped [num_pages, num_kv_heads, page_size, 128].
 """
 
@@ -20,7 +22,7 @@ import os
 __all__ = [
     "QilError", "lib_path", "load", "version", "kv_write", "QKNormRope", "rope_cos_sin",
     "paged_decode", "paged_decode_workspace_size", "paged_prefill", "paged_attention_mixed",
-    "set_debug", "debug_enabled",
+    "qkv_proj_write", "set_debug", "debug_enabled",
     "QIL_F32", "QIL_BF16",
 ]
 
@@ -93,6 +95,9 @@ def load(path=None):
     lib.qil_kv_write.restype = ctypes.c_int
     lib.qil_kv_write.argtypes = [vp, vp, i64, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                  ctypes.POINTER(_QKNormRopeC), vp]
+    lib.qil_qkv_proj_write.restype = ctypes.c_int
+    lib.qil_qkv_proj_write.argtypes = [vp, i64, vp, i64, i32, vp, vp, vp, vp, vp, i32, i32, i32,
+                                       i32, i32, i32, vp, vp, f32, vp, vp, i32, i32, vp]
     lib.qil_rope_cos_sin.restype = ctypes.c_int
     lib.qil_rope_cos_sin.argtypes = [vp, i32, i32, ctypes.c_double, vp]
     lib.qil_paged_decode_workspace_size.restype = sz
@@ -196,6 +201,30 @@ def kv_write(k, v, k_cache, v_cache, slot_mapping, fuse=None, stream=None):
         _ptr(k), _ptr(v), _token_stride(k, hkv * d), _token_stride(v, hkv * d),
         _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), int(slot_mapping.shape[0]), hkv, d,
         page, num_pages, _dtype_code(k_cache), c_fuse, _stream(stream))
+    _check(rc)
+
+
+def qkv_proj_write(x, weight, k_cache, v_cache, slot_mapping, q_out, num_q_heads,
+                   q_norm_weight, k_norm_weight, positions, cos_sin, eps=1e-6, qkv_out=None,
+                   stream=None):
+    """The merged QKV projection x @ weight^T (x [T, hidden], weight
+    [(Hq + 2 Hkv) * 128, hidden], bf16) with the fused Q/K RMSNorm + RoPE +
+    scatter write as its epilogue: rotated q rows to q_out [T, Hq, 128],
+    rotated k and projected v rows into the pools through slot_mapping.
+    qkv_out ([T, (Hq + 2 Hkv) * 128]) optionally receives the rounded
+    projection."""
+    num_pages, hkv, page, d = _pool_shape(k_cache)
+    if x.dim() != 2 or weight.dim() != 2 or x.stride(1) != 1 or weight.stride(1) != 1:
+        raise QilError(1, "x and weight must be 2-D with contiguous rows")
+    hidden = int(x.shape[1])
+    if int(weight.shape[1]) != hidden or int(weight.shape[0]) != (num_q_heads + 2 * hkv) * d:
+        raise QilError(1, f"weight must be [{(num_q_heads + 2 * hkv) * d}, {hidden}]")
+    rc = load().qil_qkv_proj_write(
+        _ptr(x), int(x.stride(0)), _ptr(weight), int(weight.stride(0)), hidden, _ptr(q_out),
+        _ptr(qkv_out), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), int(x.shape[0]),
+        int(num_q_heads), hkv, d, page, num_pages, _ptr(q_norm_weight), _ptr(k_norm_weight),
+        float(eps), _ptr(positions), _ptr(cos_sin), int(cos_sin.shape[0]), _dtype_code(x),
+        _stream(stream))
     _check(rc)
 
 

@@ -21,7 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqil.so")
 ARCH = os.environ.get("QIL_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.hip", "kv_write.hip", "decode.hip", "prefill.hip", "mixed.hip", "debug_check.hip"]
+SOURCES = ["api.hip", "kv_write.hip", "qkv_proj.hip", "decode.hip", "prefill.hip", "mixed.hip",
+           "debug_check.hip"]
 # measured-ceiling kernels for the benchmark, in a library of their own
 CEILING_SOURCE = "ceiling.hip"
 CEILING_LIB = os.path.join(PKG, "libqil_ceiling.so")

@@ -393,6 +393,63 @@ int qil_kv_write(const void* k, const void* v, int64_t k_token_stride, int64_t v
   return ok();
 }
 
+int qil_qkv_proj_write(const void* x, int64_t x_token_stride, const void* weight,
+                       int64_t weight_row_stride, int32_t hidden, void* q_out, void* qkv_out,
+                       void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                       int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t page_size, int32_t num_pages,
+                       const void* q_norm_weight, const void* k_norm_weight, float eps,
+                       const int32_t* positions, const float* cos_sin, int32_t max_position,
+                       int32_t dtype, void* stream) {
+  if (num_tokens < 0) return fail(QIL_EINVAL, "num_tokens %d < 0", num_tokens);
+  if (dtype != QIL_BF16) return fail(QIL_EUNSUPPORTED, "the QKV projection is bf16 only");
+  if (num_kv_heads <= 0 || num_q_heads <= 0)
+    return fail(QIL_EINVAL, "head counts must be positive (q %d, kv %d)", num_q_heads, num_kv_heads);
+  if ((num_q_heads + 2 * num_kv_heads) % 2)
+    return fail(QIL_EUNSUPPORTED, "num_q_heads + 2*num_kv_heads = %d is odd",
+                num_q_heads + 2 * num_kv_heads);
+  if (head_dim != qil::kHeadDim) return fail(QIL_EUNSUPPORTED, "head_dim %d not built (128)", head_dim);
+  if (log2_page_size(page_size) < 0)
+    return fail(QIL_EUNSUPPORTED, "page_size %d not built (16, 32, 64, 128, 256)", page_size);
+  if (num_pages <= 0) return fail(QIL_EINVAL, "num_pages must be positive (%d)", num_pages);
+  if (hidden <= 0 || hidden % 64)
+    return fail(QIL_EUNSUPPORTED, "hidden %d is not a positive multiple of 64", hidden);
+  if (x_token_stride < hidden || weight_row_stride < hidden || x_token_stride % 8 ||
+      weight_row_stride % 8)
+    return fail(QIL_EINVAL, "strides (%lld, %lld) must be >= hidden %d and multiples of 8",
+                (long long)x_token_stride, (long long)weight_row_stride, hidden);
+  if (max_position <= 0) return fail(QIL_EINVAL, "max_position must be positive");
+  if (!(eps >= 0.f)) return fail(QIL_EINVAL, "eps must be >= 0");
+  if ((int64_t)num_pages * page_size > INT32_MAX)
+    return fail(QIL_EINVAL, "num_pages*page_size exceeds the int32 slot range");
+  if (num_tokens == 0) return ok();
+  if (!x || !weight || !q_out || !k_cache || !v_cache || !slot_mapping || !q_norm_weight ||
+      !k_norm_weight || !positions || !cos_sin)
+    return fail(QIL_EINVAL, "null pointer argument");
+  if (!aligned16(x) || !aligned16(weight) || !aligned16(q_out) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(q_norm_weight) || !aligned16(k_norm_weight) ||
+      !aligned16(cos_sin) || (qkv_out && !aligned16(qkv_out)))
+    return fail(QIL_EINVAL, "tensors must be 16-byte aligned");
+
+  qil::QkvProjArgs a{x, x_token_stride, weight, weight_row_stride, hidden, num_tokens,
+                     num_q_heads, num_kv_heads, q_out, qkv_out, k_cache, v_cache, slot_mapping,
+                     log2_page_size(page_size), num_pages, q_norm_weight, k_norm_weight, eps,
+                     positions, cos_sin, max_position};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_on()) {
+    const int64_t num_slots = (int64_t)num_pages * page_size;
+    int rc = run_checks(s, [&](qil::DebugReport* rep) {
+      hipError_t e = qil::launch_check_slots(slot_mapping, num_tokens, num_slots, rep, s);
+      if (e == hipSuccess) e = qil::launch_check_positions(positions, num_tokens, max_position, rep, s);
+      return e;
+    });
+    if (rc) return rc;
+  }
+  hipError_t e = qil::launch_qkv_proj(a, s);
+  if (e != hipSuccess) return fail(QIL_EHIP, "qkv projection launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int qil_rope_cos_sin(float* cos_sin, int32_t max_position, int32_t head_dim, double theta,
                      void* stream) {
   if (!cos_sin) return fail(QIL_EINVAL, "null table");

@@ -44,6 +44,33 @@ hipError_t launch_kv_write_fused(const KvWriteArgs& a, const FusedArgs& f, hipSt
 hipError_t launch_rope_table(float* table, int32_t max_position, int32_t head_dim, double theta,
                              hipStream_t s);
 
+// ---- merged QKV projection + fused norm / RoPE / scatter (bf16) -----------
+struct QkvProjArgs {
+  const void* x;          // [num_tokens] rows of `hidden` values, stride x_stride
+  int64_t x_stride;       // elements
+  const void* weight;     // [(Hq + 2 Hkv) * 128] rows of `hidden` values, stride weight_stride
+  int64_t weight_stride;  // elements
+  int32_t hidden;         // multiple of 64
+  int32_t num_tokens;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  void* q_out;            // [num_tokens][Hq][128]
+  void* qkv_out;          // [num_tokens][(Hq + 2 Hkv) * 128] or null
+  void* k_cache;
+  void* v_cache;
+  const int32_t* slots;
+  int32_t log2_page;
+  int32_t num_pages;
+  const void* q_w;
+  const void* k_w;
+  float eps;
+  const int32_t* positions;
+  const float* cos_sin;
+  int32_t max_position;
+};
+
+hipError_t launch_qkv_proj(const QkvProjArgs& a, hipStream_t s);
+
 // ---- decode ----------------------------------------------------------------
 struct DecodeArgs {
   void* out;

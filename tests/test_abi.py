@@ -70,6 +70,36 @@ def test_kv_write_validation(lib):
     assert kvw(lib, fuse=ctypes.pointer(f4)) == EINVAL           # null weight
 
 
+def qkvp(lib, **kw):
+    a = dict(x=FAKE, xs=4096, w=FAKE, ws=4096, hidden=4096, q_out=FAKE, qkv=None, kc=FAKE, vc=FAKE,
+             slots=FAKE, T=4, hq=32, hkv=8, d=128, page=16, pages=10, qw=FAKE, kw=FAKE, eps=1e-6,
+             pos=FAKE, cs=FAKE, maxpos=8192, dtype=1)
+    a.update(kw)
+    return lib.qil_qkv_proj_write(a["x"], a["xs"], a["w"], a["ws"], a["hidden"], a["q_out"],
+                                  a["qkv"], a["kc"], a["vc"], a["slots"], a["T"], a["hq"], a["hkv"],
+                                  a["d"], a["page"], a["pages"], a["qw"], a["kw"], a["eps"],
+                                  a["pos"], a["cs"], a["maxpos"], a["dtype"], None)
+
+
+def test_qkv_proj_validation(lib):
+    assert qkvp(lib, T=0) == 0                     # no-op, no HIP call
+    assert qkvp(lib, T=-1) == EINVAL
+    assert qkvp(lib, dtype=0) == EUNSUP            # bf16 only
+    assert qkvp(lib, hq=31) == EUNSUP              # 31 + 16 heads: odd
+    assert qkvp(lib, hidden=4000, xs=4000, ws=4000) == EUNSUP   # not a multiple of 64
+    assert qkvp(lib, xs=4088) == EINVAL            # stride below hidden
+    assert qkvp(lib, ws=4100) == EINVAL            # stride not a multiple of 8
+    assert qkvp(lib, d=64) == EUNSUP
+    assert qkvp(lib, page=8) == EUNSUP
+    assert qkvp(lib, pages=0) == EINVAL
+    assert qkvp(lib, maxpos=0) == EINVAL
+    assert qkvp(lib, eps=-1.0) == EINVAL
+    assert qkvp(lib, x=None) == EINVAL
+    assert qkvp(lib, kw=None) == EINVAL
+    assert qkvp(lib, w=FAKE + 8) == EINVAL         # misaligned
+    assert qkvp(lib, qkv=FAKE + 2) == EINVAL       # misaligned optional output
+
+
 def dec(lib, **kw):
     a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, bts=128, ctx=FAKE, B=2, hq=16, hkv=8,
              d=128, page=16, pages=8192, maxL=2048, scale=0.088, dtype=1, S=0, ws=None, wsb=0)
