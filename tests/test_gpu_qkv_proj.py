@@ -113,6 +113,7 @@ def small_case(seed, hidden, hq, hkv, ntok, page=16, drop=()):
     (128, 16, 8, 130, 8),    # two stages, a token stride above hidden
     (192, 32, 8, 129, 0),    # three stages, 8B head counts
     (1024, 40, 8, 200, 0),   # 14B head counts (28 head pairs), 0.6B hidden size
+    (1024, 16, 8, 1100, 0),  # 256-token workgroups (from 1024 tokens), ragged last tile
 ])
 def test_small_shapes(qil, hidden, hq, hkv, ntok, x_pad):
     print(f"qkv_proj hidden={hidden} hq={hq} hkv={hkv} tokens={ntok}", flush=True)
