@@ -697,9 +697,12 @@ def cpu_baseline(seconds):
                                    f"first), {pflops / 1e9:.1f} causal GFLOP in {pbusy:.1f} s"})
 
 
+# every source file a kernel is compiled from (its launcher, its body and the
+# shared headers): traffic figures are used only while all are unchanged
 KERNEL_SOURCES = {
-    "decode-b256": ("decode.hip", "decode_body.h"),
-    "prefill-varlen": ("prefill.hip", "prefill_body.h"),
+    "decode-b256": ("decode.hip", "decode_body.h", "device_common.h", "qil_internal.h"),
+    "prefill-varlen": ("prefill.hip", "prefill_body.h", "device_common.h", "qil_internal.h"),
+    "qkv-proj-8b": ("qkv_proj.hip", "device_common.h", "qil_internal.h"),
 }
 
 
@@ -853,6 +856,7 @@ def main():
             "bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
             "flops": int(qp["flops"]), "launch_us": round(qp["fused_ms"] * 1e3, 2),
+            "traffic": traffic_for("qkv-proj-8b"),
             "library_gemm_then_fused_write_us": {
                 "gemm": round(qp["gemm_ms"] * 1e3, 2), "fused_write": round(qp["write_ms"] * 1e3, 2),
                 "total": round((qp["gemm_ms"] + qp["write_ms"]) * 1e3, 2)}}
