@@ -219,7 +219,13 @@ int qil_qkv_proj_write(const void* x, int64_t x_token_stride, const void* weight
  *                  kernel through the log-sum-exp rule.
  *   workspace      device scratch of at least
  *                  qil_paged_decode_workspace_size(...) bytes (may be NULL when
- *                  that size is 0); its contents on entry do not matter.
+ *                  that size is 0); its contents on entry do not matter.  It
+ *                  holds the split partials when a request spans several
+ *                  splits, and, when the grid has at least 512 workgroups
+ *                  (batch * num_kv_heads * splits), the order in which the
+ *                  requests are run: a first small kernel sorts them by
+ *                  decreasing context length so that the longest start first.
+ *                  Results do not depend on that order.
  * batch == 0 is a no-op.
  */
 size_t qil_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -176,12 +176,30 @@ SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t max_context_l
   return p;
 }
 
-size_t workspace_bytes_for(int32_t batch, int32_t num_q_heads, const SplitPlan& p) {
+// Decode grids of at least this many workgroups (two rounds of 256 CUs at
+// two workgroups per CU, and more) run their requests longest first, through
+// an order array in the workspace.  Measured at B = 256 (2,048 workgroups):
+// 171 -> 158 us with the batch sorted by decreasing context length.
+constexpr int64_t kOrderMinBlocks = 512;
+
+bool decode_ordered(int32_t batch, int32_t num_kv_heads, const SplitPlan& p) {
+  return (int64_t)batch * num_kv_heads * p.num_splits >= kOrderMinBlocks;
+}
+
+size_t split_bytes_for(int32_t batch, int32_t num_q_heads, const SplitPlan& p) {
   if (p.num_splits <= 1) return 0;
   const size_t parts = (size_t)batch * num_q_heads * p.num_splits;
   // o[128] then m, l per part; each array rounded up to 256 bytes.
   auto up = [](size_t b) { return (b + 255) / 256 * 256; };
   return up(parts * qil::kHeadDim * 4) + 2 * up(parts * 4);
+}
+
+// Workspace: the split partials (when there are several splits), then the
+// request order (when the grid is large enough to run longest first).
+size_t workspace_bytes_for(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                           const SplitPlan& p) {
+  const size_t order = decode_ordered(batch, num_kv_heads, p) ? ((size_t)batch * 4 + 255) / 256 * 256 : 0;
+  return split_bytes_for(batch, num_q_heads, p) + order;
 }
 
 hipError_t check_decode_metadata(const qil::DecodeArgs& a, qil::DebugReport* rep, hipStream_t s) {
@@ -233,7 +251,7 @@ int prep_decode(void* out, const void* q, const void* k_cache, const void* v_cac
   if (p.num_splits > kMaxSplits)
     return fail(QIL_EINVAL, "max_context_len %d needs %d splits (at most %d)", max_context_len,
                 p.num_splits, kMaxSplits);
-  const size_t need = workspace_bytes_for(batch, num_q_heads, p);
+  const size_t need = workspace_bytes_for(batch, num_q_heads, num_kv_heads, p);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return fail(QIL_EWORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -266,6 +284,9 @@ int prep_decode(void* out, const void* q, const void* k_cache, const void* v_cac
     a.ws_m = reinterpret_cast<float*>(base + up(parts * qil::kHeadDim * 4));
     a.ws_l = reinterpret_cast<float*>(base + up(parts * qil::kHeadDim * 4) + up(parts * 4));
   }
+  if (decode_ordered(batch, num_kv_heads, p))
+    a.order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                         split_bytes_for(batch, num_q_heads, p));
   return QIL_OK;
 }
 
@@ -470,7 +491,7 @@ size_t qil_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32
   if (keys_per_split < 0 || keys_per_split % 64 || keys_per_split > kMaxKeysPerSplit) return 0;
   const SplitPlan p = plan_splits(batch, num_kv_heads, max_context_len, keys_per_split);
   if (p.num_splits > kMaxSplits) return 0;
-  return workspace_bytes_for(batch, num_q_heads, p);
+  return workspace_bytes_for(batch, num_q_heads, num_kv_heads, p);
 }
 
 int qil_paged_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -535,6 +556,7 @@ int qil_paged_attention_mixed(const qil_decode_batch* decode, const qil_prefill_
                      dtype, decode->keys_per_split, decode->workspace, decode->workspace_bytes, da,
                      &dec_empty);
     if (rc) return rc;
+    da.order = nullptr;  // the mixed grid deals out its decode splits itself
   }
   if (prefill) {
     rc = prep_prefill(prefill->out, prefill->q, k_cache, v_cache, prefill->block_tables,

@@ -73,7 +73,7 @@ template <int G>
 __global__ __launch_bounds__(64 * kFW) void decode_f32_kernel(DecodeArgs a) {
   const int split = blockIdx.x;
   const int g = blockIdx.y;
-  const int r = blockIdx.z;
+  const int r = a.order != nullptr ? a.order[blockIdx.z] : (int)blockIdx.z;
   const int L = min(a.context_lens[r], a.max_context_len);
   const int kbeg = split * a.keys_per_split;
   if (kbeg >= L) return;  // this split lies past the context (uniform per block)
@@ -299,8 +299,55 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a) {
     static_cast<float*>(a.out)[oi] = val;
 }
 
+// Longest requests first.  Workgroups are dispatched in grid order, and when
+// the grid takes several rounds of the GPU, a long context started last
+// leaves the GPU idle around it while it finishes.  One workgroup sorts the
+// requests into 256 buckets of decreasing context length (counting sort with
+// LDS atomics; the order inside a bucket does not matter, since every
+// request's result is independent of which workgroup computes it) and
+// writes the permutation that the decode grid reads its request ids through.
+constexpr int kOrderBuckets = 256;
+constexpr int kOrderThreads = 1024;
+
+__global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(const int32_t* context_lens,
+                                                                     int batch, int max_len,
+                                                                     int32_t* order) {
+  __shared__ int hist[kOrderBuckets];
+  __shared__ int scan[2][kOrderBuckets];
+  const int tid = threadIdx.x;
+  auto bucket = [&](int r) {
+    int L = context_lens[r];
+    L = L < 0 ? 0 : (L > max_len ? max_len : L);
+    return (int)((int64_t)(max_len - L) * kOrderBuckets / ((int64_t)max_len + 1));  // 0 = longest
+  };
+  if (tid < kOrderBuckets) hist[tid] = 0;
+  __syncthreads();
+  for (int r = tid; r < batch; r += kOrderThreads) atomicAdd(&hist[bucket(r)], 1);
+  __syncthreads();
+  // inclusive prefix sum of the bucket counts (Hillis-Steele, 8 steps)
+  if (tid < kOrderBuckets) scan[0][tid] = hist[tid];
+  __syncthreads();
+  int src = 0;
+  for (int off = 1; off < kOrderBuckets; off <<= 1) {
+    if (tid < kOrderBuckets)
+      scan[src ^ 1][tid] = scan[src][tid] + (tid >= off ? scan[src][tid - off] : 0);
+    __syncthreads();
+    src ^= 1;
+  }
+  // first free position of each bucket
+  if (tid < kOrderBuckets) hist[tid] = scan[src][tid] - hist[tid];
+  __syncthreads();
+  for (int r = tid; r < batch; r += kOrderThreads) order[atomicAdd(&hist[bucket(r)], 1)] = r;
+}
+
 template <int G, bool BF16>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
+  if (a.order != nullptr) {
+    hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderThreads), 0, s, a.context_lens,
+                       a.batch, a.max_context_len, a.order);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
   if constexpr (BF16)
     hipLaunchKernelGGL((decode_mfma_kernel<G>), grid, dim3(64 * kMW), 0, s, a);

@@ -283,7 +283,8 @@ __device__ __forceinline__ void decode_mfma_split(const DecodeArgs& a, int split
 template <int G>
 __global__ __launch_bounds__(64 * kMW) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) DecodeRing smem[kMW];
-  decode_mfma_split<G, kMW>(a, blockIdx.x, blockIdx.y, blockIdx.z, smem);
+  const int r = a.order != nullptr ? a.order[blockIdx.z] : (int)blockIdx.z;
+  decode_mfma_split<G, kMW>(a, blockIdx.x, blockIdx.y, r, smem);
 }
 
 }  // namespace

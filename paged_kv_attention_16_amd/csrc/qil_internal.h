@@ -92,6 +92,8 @@ struct DecodeArgs {
   float* ws_o;             // [batch][Hq][num_splits][128]   (num_splits > 1)
   float* ws_m;             // [batch][Hq][num_splits]
   float* ws_l;             // [batch][Hq][num_splits]
+  int32_t* order;          // [batch] requests by decreasing context length, or null
+                           // (then request r is grid row r)
   bool bf16;
 };
 

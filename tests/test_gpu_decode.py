@@ -50,6 +50,25 @@ def test_split_invariance(qil, split):
     assert H.excess(forced[:4], ref, "bf16") <= 0
 
 
+@pytest.mark.parametrize("split", [256, 4096])
+def test_longest_first_order_is_invisible(qil, split):
+    """The B = 256 workload's grid (2,048 workgroups and more) runs its
+    requests longest first; each request's output equals, bit for bit, the
+    same request decoded in a batch of 4, whose small grid runs in batch
+    order (the split size is fixed, so both use the same splits)."""
+    w = make_workload(3)
+    case = H.DeviceCase(w, DEV)
+    full = H.to_bits(case.decode(keys_per_split=split))
+    rng = np.random.default_rng(4)
+    L = w.context_lens
+    groups = [[int(np.argmax(L)), int(np.argmin(L)), 7, 200]] + \
+             [sorted(rng.choice(w.batch, 4, replace=False).tolist()) for _ in range(5)]
+    for grp in groups:
+        small = H.to_bits(case.decode(requests=grp, keys_per_split=split))
+        assert np.array_equal(full[grp], small), grp
+    print(f"split {split}: {len(groups)} groups of 4 match the full batch bit for bit", flush=True)
+
+
 def test_run_twice_bitwise(qil):
     w = make_workload(2)
     case = H.DeviceCase(w, DEV)
