@@ -769,7 +769,9 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "qil_paged_decode (decode_mfma_kernel<2>; one split per request, no merge pass)",
+            "kernel": "qil_paged_decode: decode_order_kernel (longest requests first) then "
+                      "decode_mfma_kernel<2>, one split per request, no merge pass; the launch "
+                      "time covers both",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
