@@ -10,21 +10,28 @@
 // bf16 as the layer's output; the epilogue then applies the same arithmetic
 // as the fused qil_kv_write to those rounded rows.
 //
-// Work split: one workgroup (4 wavefronts) owns 128 tokens x 2 output heads
-// (256 weight rows).  Each wavefront owns one head (128 columns) x 64 tokens
-// and computes the transposed block C^T = W X^T on v_mfma_f32_32x32x16_bf16
-// with the head's columns on the M side and tokens on the N side.  That
-// puts one token per lane and, for each lane, 64 of the head's 128 values
-// (the other 64 sit in lane l ^ 32): the RMSNorm sum of squares closes with
-// one cross-half swap, and a value's RoPE partner (column + 64) sits in the
-// same lane, two 32-row blocks further on.
+// Work split: a workgroup owns 2 output heads (256 weight rows) and 64 TG
+// tokens, one wavefront per (head, 64 tokens): TG = 4 (256 tokens, 8
+// wavefronts) for large batches, TG = 2 (128 tokens, 4 wavefronts) for
+// small ones.  Each wavefront computes the transposed block C^T = W X^T on
+// v_mfma_f32_32x32x16_bf16 with the head's columns on the M side and tokens
+// on the N side.  That puts one token per lane and, for each lane, 64 of the
+// head's 128 values (the other 64 sit in lane l ^ 32): the RMSNorm sum of
+// squares closes with one cross-half swap, and a value's RoPE partner
+// (column + 64) sits in the same lane, two 32-row blocks further on.
 //
 //   * Both operands are K-contiguous (x rows and nn.Linear weight rows), so
 //     64-value slices of rows go from memory straight into LDS with
 //     global_load_lds (16 bytes per lane), 16-byte chunks XOR-swizzled per
 //     row so that 16 lanes reading one chunk column hit 16 distinct bank
-//     groups.  A three-stage ring keeps two slices in flight while one is
-//     multiplied; one barrier per slice.
+//     groups.  A ring of three (TG = 2) or two (TG = 4) slices keeps the next
+//     slices in flight while one is multiplied; one barrier per slice.
+//   * The slice's LDS reads are inline assembly with counted waits, so the
+//     next k-step's operands are read while the current k-step's matrix
+//     instructions run.
+//   * The epilogue stages through LDS: the cos / sin rows of the
+//     workgroup's tokens arrive by coalesced DMA, and each wavefront's output
+//     rows leave as whole 256-byte rows.
 //   * Workgroups are numbered head pair fastest.  They are dealt to the 8
 //     XCDs round robin, so with a multiple of 8 head pairs each XCD always
 //     serves the same head pairs and streams their weight rows through its
