@@ -688,13 +688,37 @@ def cpu_baseline(seconds):
         c, n = int(w4.cached_lens[r]), int(w4.new_lens[r])
         pflops += (n * (c + 1) + n * (n - 1) // 2) * w4.num_q_heads * 4 * w4.head_dim
         pdone += 1
+    # the QKV projection + fused write of the first 256 tokens of the
+    # Qwen3-8B-shaped step (fp64 matmul of the bf16 inputs, then the fused
+    # write), as GFLOP/s of the projection
+    from oracle import norm_rope as o_nr
+    from oracle import projection as o_proj
+    w5 = make_workload(5)
+    ntok = 256
+    xb, wb = w5.projection_inputs(4096)
+    xb = xb[:ntok]
+    qw, kw = w5.norm_weights()
+    table = o_nr.rope_table(w5.max_position, w5.head_dim, w5.theta)
+    kp5 = sentinel_pool(w5.num_pages, w5.num_kv_heads, w5.page_size, w5.head_dim, w5.dtype)
+    vp5 = sentinel_pool(w5.num_pages, w5.num_kv_heads, w5.page_size, w5.head_dim, w5.dtype)
+    t0 = time.perf_counter()
+    o_proj.qkv_proj_write(kp5, vp5, xb, wb, w5.num_q_heads, w5.num_kv_heads,
+                          w5.slot_mapping_new()[:ntok], w5.positions_new()[:ntok], qw, kw, w5.eps,
+                          table, w5.page_size)
+    qbusy = time.perf_counter() - t0
+    qflops = 2 * ntok * wb.shape[0] * 4096
+    del kp5, vp5
     return dict(value=nbytes / busy / 1e9, unit="GB/s", cores=cores, kind="oracle",
                 sample=f"decode-b256 step, all {w.batch} requests (scatter write + fp64 decode over "
                        f"{nbytes / 1e6:.0f} MB of K/V), {busy:.1f} s on the host; "
                        f"{len(os.sched_getaffinity(0))} usable cores",
                 prefill={"value": pflops / max(pbusy, 1e-9) / 1e9, "unit": "GFLOP/s",
                          "sample": f"{pdone} of {w4.batch} prefill-varlen requests (shortest chunks "
-                                   f"first), {pflops / 1e9:.1f} causal GFLOP in {pbusy:.1f} s"})
+                                   f"first), {pflops / 1e9:.1f} causal GFLOP in {pbusy:.1f} s"},
+                qkv_proj={"value": qflops / max(qbusy, 1e-9) / 1e9, "unit": "GFLOP/s",
+                          "sample": f"{ntok} of {int(w5.new_lens.sum())} qkv-proj-8b tokens "
+                                    f"(fp64 projection + fused write), {qflops / 1e9:.1f} GFLOP "
+                                    f"in {qbusy:.2f} s"})
 
 
 # every source file a kernel is compiled from (its launcher, its body and the
