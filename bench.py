@@ -539,13 +539,30 @@ def qkv_proj_leg(args, dev, stream, flush):
         fused_ms = flushed_kernel_ms(fused, args, flush, stream)
         gemm_ms = flushed_kernel_ms(gemm, args, flush, stream)
         write_ms = flushed_kernel_ms(write, args, flush, stream)
+        # the decode-only step of the same model: its 64 tokens (split path)
+        d = 64
+        xd, qd, qkvd = x[:d], q_out[:d], qkv[:d]
+        sd, pd = slots[:d], pos[:d]
+        wsd = torch.empty(max(qil.qkv_proj_workspace_size(d, hq, hkv, hidden), 1),
+                          dtype=torch.uint8, device=dev)
+        fused_d = lambda: qil.qkv_proj_write(xd, wt, kp, vp, sd, qd, hq, qw, kw, pd, table,
+                                             eps=w5.eps, workspace=wsd, stream=stream)
+        gemm_d = lambda: torch.matmul(xd, wt.t(), out=qkvd)
+        fuse_d = qil.QKNormRope(qkvd[:, :hq * 128], qd, qw, kw, pd, table, eps=w5.eps, num_q_heads=hq)
+        write_d = lambda: qil.kv_write(qkvd[:, hq * 128:(hq + hkv) * 128], qkvd[:, (hq + hkv) * 128:],
+                                       kp, vp, sd, fuse=fuse_d, stream=stream)
+        fused_d_ms = flushed_kernel_ms(fused_d, args, flush, stream)
+        lib_d_ms = flushed_kernel_ms(gemm_d, args, flush, stream) + \
+            flushed_kernel_ms(write_d, args, flush, stream)
     flops = 2 * t * n * hidden
     tf = flops / (fused_ms * 1e-3) / 1e12
     print(f"[bench] qkv-proj-8b: one kernel {fused_ms*1e3:.1f} us ({tf:.0f} TFLOP/s); "
-          f"library GEMM {gemm_ms*1e3:.1f} us + fused write {write_ms*1e3:.1f} us", flush=True)
+          f"library GEMM {gemm_ms*1e3:.1f} us + fused write {write_ms*1e3:.1f} us; "
+          f"64-token decode step: {fused_d_ms*1e3:.1f} us vs {lib_d_ms*1e3:.1f} us", flush=True)
     del kp, vp
     torch.cuda.empty_cache()
-    return dict(tokens=t, flops=flops, fused_ms=fused_ms, gemm_ms=gemm_ms, write_ms=write_ms)
+    return dict(tokens=t, flops=flops, fused_ms=fused_ms, gemm_ms=gemm_ms, write_ms=write_ms,
+                decode_step_ms=fused_d_ms, decode_step_library_ms=lib_d_ms)
 
 
 def measured_ceilings(dev, stream):
@@ -885,7 +902,10 @@ def main():
             "traffic": traffic_for("qkv-proj-8b"),
             "library_gemm_then_fused_write_us": {
                 "gemm": round(qp["gemm_ms"] * 1e3, 2), "fused_write": round(qp["write_ms"] * 1e3, 2),
-                "total": round((qp["gemm_ms"] + qp["write_ms"]) * 1e3, 2)}}
+                "total": round((qp["gemm_ms"] + qp["write_ms"]) * 1e3, 2)},
+            "decode_step_64_tokens_us": {
+                "one_kernel_split": round(qp["decode_step_ms"] * 1e3, 2),
+                "library_gemm_then_fused_write": round(qp["decode_step_library_ms"] * 1e3, 2)}}
     if "shard" in res:
         line["tp8_shard_decode"] = res["shard"]
     if not args.skip_cpu:

@@ -189,9 +189,19 @@ int qil_rope_cos_sin(float* cos_sin, int32_t max_position, int32_t head_dim, dou
  *   k_cache/v_cache, slot_mapping, page_size, num_pages: as for qil_kv_write
  *   q_norm_weight, k_norm_weight, eps, positions, cos_sin, max_position:
  *                   as in qil_qknorm_rope
+ *   workspace       device scratch of at least qil_qkv_proj_workspace_size(...)
+ *                   bytes, 16-byte aligned (may be NULL when that size is 0).
+ *                   Small batches (below 1024 tokens, when the grid of whole
+ *                   heads would be small) split the hidden dimension: fp32
+ *                   partial sums go here and a second kernel adds them in a
+ *                   fixed order before the epilogue.  Contents on entry do not
+ *                   matter.
  * Hq + 2 Hkv must be even (workgroups own pairs of heads).  Outputs must not
  * overlap the inputs.  num_tokens == 0 is a no-op.
  */
+size_t qil_qkv_proj_workspace_size(int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t hidden);
+
 int qil_qkv_proj_write(const void* x, int64_t x_token_stride, const void* weight,
                        int64_t weight_row_stride, int32_t hidden, void* q_out, void* qkv_out,
                        void* k_cache, void* v_cache, const int32_t* slot_mapping,
@@ -199,7 +209,7 @@ int qil_qkv_proj_write(const void* x, int64_t x_token_stride, const void* weight
                        int32_t head_dim, int32_t page_size, int32_t num_pages,
                        const void* q_norm_weight, const void* k_norm_weight, float eps,
                        const int32_t* positions, const float* cos_sin, int32_t max_position,
-                       int32_t dtype, void* stream);
+                       void* workspace, size_t workspace_bytes, int32_t dtype, void* stream);
 
 /*
  * qil_paged_decode -- one query token per request over its paged context

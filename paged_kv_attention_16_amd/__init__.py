@@ -22,7 +22,7 @@ import os
 __all__ = [
     "QilError", "lib_path", "load", "version", "kv_write", "QKNormRope", "rope_cos_sin",
     "paged_decode", "paged_decode_workspace_size", "paged_prefill", "paged_attention_mixed",
-    "qkv_proj_write", "set_debug", "debug_enabled",
+    "qkv_proj_write", "qkv_proj_workspace_size", "set_debug", "debug_enabled",
     "QIL_F32", "QIL_BF16",
 ]
 
@@ -97,7 +97,9 @@ def load(path=None):
                                  ctypes.POINTER(_QKNormRopeC), vp]
     lib.qil_qkv_proj_write.restype = ctypes.c_int
     lib.qil_qkv_proj_write.argtypes = [vp, i64, vp, i64, i32, vp, vp, vp, vp, vp, i32, i32, i32,
-                                       i32, i32, i32, vp, vp, f32, vp, vp, i32, i32, vp]
+                                       i32, i32, i32, vp, vp, f32, vp, vp, i32, vp, sz, i32, vp]
+    lib.qil_qkv_proj_workspace_size.restype = sz
+    lib.qil_qkv_proj_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.qil_rope_cos_sin.restype = ctypes.c_int
     lib.qil_rope_cos_sin.argtypes = [vp, i32, i32, ctypes.c_double, vp]
     lib.qil_paged_decode_workspace_size.restype = sz
@@ -204,9 +206,13 @@ def kv_write(k, v, k_cache, v_cache, slot_mapping, fuse=None, stream=None):
     _check(rc)
 
 
+def qkv_proj_workspace_size(num_tokens, num_q_heads, num_kv_heads, hidden):
+    return int(load().qil_qkv_proj_workspace_size(num_tokens, num_q_heads, num_kv_heads, hidden))
+
+
 def qkv_proj_write(x, weight, k_cache, v_cache, slot_mapping, q_out, num_q_heads,
                    q_norm_weight, k_norm_weight, positions, cos_sin, eps=1e-6, qkv_out=None,
-                   stream=None):
+                   workspace=None, stream=None):
     """The merged QKV projection x @ weight^T (x [T, hidden], weight
     [(Hq + 2 Hkv) * 128, hidden], bf16) with the fused Q/K RMSNorm + RoPE +
     scatter write as its epilogue: rotated q rows to q_out [T, Hq, 128],
@@ -219,12 +225,17 @@ def qkv_proj_write(x, weight, k_cache, v_cache, slot_mapping, q_out, num_q_heads
     hidden = int(x.shape[1])
     if int(weight.shape[1]) != hidden or int(weight.shape[0]) != (num_q_heads + 2 * hkv) * d:
         raise QilError(1, f"weight must be [{(num_q_heads + 2 * hkv) * d}, {hidden}]")
+    import torch
+    need = qkv_proj_workspace_size(int(x.shape[0]), int(num_q_heads), hkv, hidden)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = load().qil_qkv_proj_write(
         _ptr(x), int(x.stride(0)), _ptr(weight), int(weight.stride(0)), hidden, _ptr(q_out),
         _ptr(qkv_out), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), int(x.shape[0]),
         int(num_q_heads), hkv, d, page, num_pages, _ptr(q_norm_weight), _ptr(k_norm_weight),
-        float(eps), _ptr(positions), _ptr(cos_sin), int(cos_sin.shape[0]), _dtype_code(x),
-        _stream(stream))
+        float(eps), _ptr(positions), _ptr(cos_sin), int(cos_sin.shape[0]), _ptr(workspace), ws_bytes,
+        _dtype_code(x), _stream(stream))
     _check(rc)
 
 

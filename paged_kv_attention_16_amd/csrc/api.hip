@@ -423,6 +423,36 @@ int qil_kv_write(const void* k, const void* v, int64_t k_token_stride, int64_t v
   return ok();
 }
 
+namespace {
+// Split plan of the QKV projection (host integers only).  A workgroup holds
+// whole heads, so small batches give a grid of a few dozen workgroups, each
+// streaming a large slice of the weight; such batches split the hidden
+// dimension instead, aiming at ~256 workgroups, with at least four 64-column
+// slices per split and at most 16 splits.
+int32_t qkv_proj_splits(int32_t num_tokens, int32_t heads, int32_t hidden) {
+  if (num_tokens <= 0 || num_tokens >= 1024) return 1;
+  const int64_t blocks = (int64_t)(heads / 2) * ((num_tokens + 127) / 128);
+  if (blocks >= 128) return 1;
+  int64_t s = (256 + blocks - 1) / blocks;
+  const int64_t smax = (int64_t)(hidden / 64) / 4;
+  if (s > smax) s = smax;
+  if (s > 16) s = 16;
+  return s < 2 ? 1 : (int32_t)s;
+}
+
+size_t qkv_proj_workspace_bytes(int32_t num_tokens, int32_t heads, int32_t hidden) {
+  const int32_t s = qkv_proj_splits(num_tokens, heads, hidden);
+  return s > 1 ? (size_t)s * num_tokens * heads * qil::kHeadDim * 4 : 0;
+}
+}  // namespace
+
+size_t qil_qkv_proj_workspace_size(int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t hidden) {
+  if (num_tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || hidden <= 0 || hidden % 64)
+    return 0;
+  return qkv_proj_workspace_bytes(num_tokens, num_q_heads + 2 * num_kv_heads, hidden);
+}
+
 int qil_qkv_proj_write(const void* x, int64_t x_token_stride, const void* weight,
                        int64_t weight_row_stride, int32_t hidden, void* q_out, void* qkv_out,
                        void* k_cache, void* v_cache, const int32_t* slot_mapping,
@@ -430,7 +460,7 @@ int qil_qkv_proj_write(const void* x, int64_t x_token_stride, const void* weight
                        int32_t head_dim, int32_t page_size, int32_t num_pages,
                        const void* q_norm_weight, const void* k_norm_weight, float eps,
                        const int32_t* positions, const float* cos_sin, int32_t max_position,
-                       int32_t dtype, void* stream) {
+                       void* workspace, size_t workspace_bytes, int32_t dtype, void* stream) {
   if (num_tokens < 0) return fail(QIL_EINVAL, "num_tokens %d < 0", num_tokens);
   if (dtype != QIL_BF16) return fail(QIL_EUNSUPPORTED, "the QKV projection is bf16 only");
   if (num_kv_heads <= 0 || num_q_heads <= 0)
@@ -460,11 +490,20 @@ int qil_qkv_proj_write(const void* x, int64_t x_token_stride, const void* weight
       !aligned16(v_cache) || !aligned16(q_norm_weight) || !aligned16(k_norm_weight) ||
       !aligned16(cos_sin) || (qkv_out && !aligned16(qkv_out)))
     return fail(QIL_EINVAL, "tensors must be 16-byte aligned");
+  const int32_t heads = num_q_heads + 2 * num_kv_heads;
+  if ((int64_t)num_tokens * heads > (int64_t)1 << 31)
+    return fail(QIL_EINVAL, "num_tokens*heads exceeds 2^31 head rows per call");
+  const size_t need = qkv_proj_workspace_bytes(num_tokens, heads, hidden);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(QIL_EWORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
 
   qil::QkvProjArgs a{x, x_token_stride, weight, weight_row_stride, hidden, num_tokens,
                      num_q_heads, num_kv_heads, q_out, qkv_out, k_cache, v_cache, slot_mapping,
                      log2_page_size(page_size), num_pages, q_norm_weight, k_norm_weight, eps,
-                     positions, cos_sin, max_position};
+                     positions, cos_sin, max_position,
+                     qkv_proj_splits(num_tokens, heads, hidden),
+                     need > 0 ? static_cast<float*>(workspace) : nullptr};
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (debug_on()) {
     const int64_t num_slots = (int64_t)num_pages * page_size;

@@ -67,6 +67,8 @@ struct QkvProjArgs {
   const int32_t* positions;
   const float* cos_sin;
   int32_t max_position;
+  int32_t num_splits;     // 1: one pass; > 1: split over hidden, partial sums in `partials`
+  float* partials;        // [num_splits][num_tokens][(Hq + 2 Hkv) * 128] fp32 (num_splits > 1)
 };
 
 hipError_t launch_qkv_proj(const QkvProjArgs& a, hipStream_t s);

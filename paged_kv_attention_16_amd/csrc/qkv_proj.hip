@@ -86,7 +86,10 @@ __device__ __forceinline__ float sum_halves32(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
-template <int TG>
+// SPLIT: the workgroup covers the hidden slices of split blockIdx.z only and
+// writes its fp32 partial sums to a.partials; qkv_proj_reduce_kernel adds the
+// splits and applies the epilogue.
+template <int TG, bool SPLIT>
 __global__ __launch_bounds__(ProjCfg<TG>::kThreads) void qkv_proj_kernel(QkvProjArgs a) {
   using C = ProjCfg<TG>;
   constexpr int kPTok = C::kTok, kPStages = C::kStages, kPWInstr = C::kWInstr, kPXInstr = C::kXInstr;
@@ -101,7 +104,9 @@ __global__ __launch_bounds__(ProjCfg<TG>::kThreads) void qkv_proj_kernel(QkvProj
   const int t0 = blockIdx.y * kPTok;
   const int n0 = pair * kPCols;  // first weight row of the workgroup
   const int T = a.num_tokens;
-  const int nst = a.hidden / kPK;
+  const int nst_all = a.hidden / kPK;
+  const int sbeg = SPLIT ? (int)((int64_t)blockIdx.z * nst_all / a.num_splits) : 0;
+  const int nst = SPLIT ? (int)((int64_t)(blockIdx.z + 1) * nst_all / a.num_splits) - sbeg : nst_all;
 
   const char* xg = static_cast<const char*>(a.x);
   const char* wg = static_cast<const char*>(a.weight);
@@ -113,7 +118,7 @@ __global__ __launch_bounds__(ProjCfg<TG>::kThreads) void qkv_proj_kernel(QkvProj
   const int lpc = lane & 7;
   auto issue = [&](int st) __attribute__((always_inline)) {
     const int buf = st % kPStages;
-    const int64_t kofs = (int64_t)st * kPRowBytes;
+    const int64_t kofs = (int64_t)(sbeg + st) * kPRowBytes;
 #pragma unroll
     for (int i = 0; i < kPWInstr; ++i) {
       const int blk = kPWInstr * w + i;
@@ -237,6 +242,25 @@ __global__ __launch_bounds__(ProjCfg<TG>::kThreads) void qkv_proj_kernel(QkvProj
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     if (s + kPStages - 1 < nst) issue(s + kPStages - 1);
     compute(s);
+  }
+
+  if constexpr (SPLIT) {
+    // fp32 partial sums of this split: 4 consecutive columns per store
+    const int ncols_p = (Hq + 2 * Hkv) * kHeadDim;
+    float* part = a.partials + (int64_t)blockIdx.z * T * ncols_p + head * kHeadDim;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int t = t0 + xrow0 + 32 * nb + lq;
+      if (t >= T) continue;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<float4*>(part + (int64_t)t * ncols_p + 32 * mb + 8 * j + 4 * hf) =
+              make_float4(acc[nb][mb][4 * j], acc[nb][mb][4 * j + 1], acc[nb][mb][4 * j + 2],
+                          acc[nb][mb][4 * j + 3]);
+    }
+    return;
   }
 
   // ---- epilogue ---------------------------------------------------------
@@ -415,20 +439,128 @@ __global__ __launch_bounds__(ProjCfg<TG>::kThreads) void qkv_proj_kernel(QkvProj
   });
 }
 
+// The split path's second kernel: the epilogue for one (token, head) row per
+// 16 lanes, lane j holding columns 8 j .. 8 j + 7 (the first half of the head
+// in lanes 0-7, so a value's RoPE partner sits 8 lanes away).  It adds the
+// splits' partial sums in split order, rounds to bf16 as the layer's output,
+// and applies the same arithmetic as the fused qil_kv_write to that row.
+__global__ __launch_bounds__(256) void qkv_proj_reduce_kernel(QkvProjArgs a) {
+  const int heads = a.num_q_heads + 2 * a.num_kv_heads;
+  const int ncols = heads * kHeadDim;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int j = threadIdx.x & 15;
+  if (row >= (int64_t)a.num_tokens * heads) return;  // whole 16-lane groups exit together
+  const int t = (int)(row / heads);
+  const int head = (int)(row - (int64_t)t * heads);
+  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+  const int kind = head < Hq ? 0 : (head < Hq + Hkv ? 1 : 2);  // q, k, v
+  const int hidx = kind == 0 ? head : (kind == 1 ? head - Hq : head - Hq - Hkv);
+
+  float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const float* src = a.partials + (int64_t)t * ncols + head * kHeadDim + 8 * j;
+  const int64_t split_stride = (int64_t)a.num_tokens * ncols;
+  for (int z = 0; z < a.num_splits; ++z) {
+    const float4 lo = *reinterpret_cast<const float4*>(src + z * split_stride);
+    const float4 hi = *reinterpret_cast<const float4*>(src + z * split_stride + 4);
+    x[0] += lo.x; x[1] += lo.y; x[2] += lo.z; x[3] += lo.w;
+    x[4] += hi.x; x[5] += hi.y; x[6] += hi.z; x[7] += hi.w;
+  }
+  uint32_t px[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) px[i] = cvt_pk_bf16(x[2 * i], x[2 * i + 1]);
+  if (a.qkv_out != nullptr)
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.qkv_out) + (int64_t)t * ncols + head * kHeadDim + 8 * j) =
+        make_uint4(px[0], px[1], px[2], px[3]);
+
+  uint16_t* dst = nullptr;
+  if (kind == 0) {
+    dst = static_cast<uint16_t*>(a.q_out) + ((int64_t)t * Hq + hidx) * kHeadDim;
+  } else {
+    const int32_t slot = a.slots[t];
+    const int64_t page = slot >> a.log2_page;
+    if (slot >= 0 && page < a.num_pages) {
+      const int64_t prow = ((page * Hkv + hidx) << a.log2_page) + (slot & ((1 << a.log2_page) - 1));
+      dst = static_cast<uint16_t*>(kind == 1 ? a.k_cache : a.v_cache) + prow * kHeadDim;
+    }
+  }
+  if (kind == 2) {  // v: the rounded projection as it is
+    if (dst != nullptr) *reinterpret_cast<uint4*>(dst + 8 * j) = make_uint4(px[0], px[1], px[2], px[3]);
+    return;
+  }
+
+  // q / k: RMSNorm over the 16 lanes of the row, then RoPE
+  float xr[8], ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xr[2 * i] = bf16_lo(px[i]);
+    xr[2 * i + 1] = bf16_hi(px[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ss = fmaf(xr[i], xr[i], ss);
+  ss = row_sum16(ss);
+  const float inv_rms = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
+  const uint4 wraw = *reinterpret_cast<const uint4*>(
+      static_cast<const uint16_t*>(kind == 0 ? a.q_w : a.k_w) + 8 * j);
+  const uint32_t ww[4] = {wraw.x, wraw.y, wraw.z, wraw.w};
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // bf16(x * r), then bf16(that * w)
+    const uint32_t n = cvt_pk_bf16(xr[2 * i] * inv_rms, xr[2 * i + 1] * inv_rms);
+    const uint32_t m = cvt_pk_bf16(bf16_lo(n) * bf16_lo(ww[i]), bf16_hi(n) * bf16_hi(ww[i]));
+    y[2 * i] = bf16_lo(m);
+    y[2 * i + 1] = bf16_hi(m);
+  }
+  int pos = a.positions[t];
+  pos = pos < 0 ? 0 : (pos >= a.max_position ? a.max_position - 1 : pos);
+  const float* cs = a.cos_sin + (int64_t)pos * kHeadDim + 8 * (j & 7);
+  const float4 c0 = *reinterpret_cast<const float4*>(cs);
+  const float4 c1 = *reinterpret_cast<const float4*>(cs + 4);
+  const float4 s0 = *reinterpret_cast<const float4*>(cs + kHeadDim / 2);
+  const float4 s1 = *reinterpret_cast<const float4*>(cs + kHeadDim / 2 + 4);
+  const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  const bool first_half = j < 8;
+  uint32_t o32[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float r[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = 2 * i + h;
+      const float partner = row_swap8(y[e]);
+      // first half: y1*c - y2*s ; second half: y2*c + y1*s
+      r[h] = first_half ? (y[e] * cv[e] - partner * sv[e]) : (y[e] * cv[e] + partner * sv[e]);
+    }
+    o32[i] = cvt_pk_bf16(r[0], r[1]);
+  }
+  if (dst != nullptr) *reinterpret_cast<uint4*>(dst + 8 * j) = make_uint4(o32[0], o32[1], o32[2], o32[3]);
+}
+
 }  // namespace
 
 hipError_t launch_qkv_proj(const QkvProjArgs& a, hipStream_t s) {
   const int heads = a.num_q_heads + 2 * a.num_kv_heads;
   if (a.num_tokens == 0) return hipSuccess;
+  if (a.num_splits > 1) {
+    // split over hidden: partial sums, then their sum and the epilogue
+    dim3 grid(heads / 2, (a.num_tokens + ProjCfg<2>::kTok - 1) / ProjCfg<2>::kTok, a.num_splits);
+    hipLaunchKernelGGL((qkv_proj_kernel<2, true>), grid, dim3(ProjCfg<2>::kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t rows = (int64_t)a.num_tokens * heads;
+    hipLaunchKernelGGL(qkv_proj_reduce_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   // 256-token workgroups from 1024 tokens on (measured on the Qwen3-8B
   // shape: 2112 tokens run in one round of 216 workgroups instead of two
   // rounds of 408); smaller batches keep more, smaller workgroups
   if (a.num_tokens >= 1024) {
     dim3 grid(heads / 2, (a.num_tokens + ProjCfg<4>::kTok - 1) / ProjCfg<4>::kTok);
-    hipLaunchKernelGGL(qkv_proj_kernel<4>, grid, dim3(ProjCfg<4>::kThreads), 0, s, a);
+    hipLaunchKernelGGL((qkv_proj_kernel<4, false>), grid, dim3(ProjCfg<4>::kThreads), 0, s, a);
   } else {
     dim3 grid(heads / 2, (a.num_tokens + ProjCfg<2>::kTok - 1) / ProjCfg<2>::kTok);
-    hipLaunchKernelGGL(qkv_proj_kernel<2>, grid, dim3(ProjCfg<2>::kThreads), 0, s, a);
+    hipLaunchKernelGGL((qkv_proj_kernel<2, false>), grid, dim3(ProjCfg<2>::kThreads), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -73,12 +73,13 @@ def test_kv_write_validation(lib):
 def qkvp(lib, **kw):
     a = dict(x=FAKE, xs=4096, w=FAKE, ws=4096, hidden=4096, q_out=FAKE, qkv=None, kc=FAKE, vc=FAKE,
              slots=FAKE, T=4, hq=32, hkv=8, d=128, page=16, pages=10, qw=FAKE, kw=FAKE, eps=1e-6,
-             pos=FAKE, cs=FAKE, maxpos=8192, dtype=1)
+             pos=FAKE, cs=FAKE, maxpos=8192, work=FAKE, workb=1 << 30, dtype=1)
     a.update(kw)
     return lib.qil_qkv_proj_write(a["x"], a["xs"], a["w"], a["ws"], a["hidden"], a["q_out"],
                                   a["qkv"], a["kc"], a["vc"], a["slots"], a["T"], a["hq"], a["hkv"],
                                   a["d"], a["page"], a["pages"], a["qw"], a["kw"], a["eps"],
-                                  a["pos"], a["cs"], a["maxpos"], a["dtype"], None)
+                                  a["pos"], a["cs"], a["maxpos"], a["work"], a["workb"],
+                                  a["dtype"], None)
 
 
 def test_qkv_proj_validation(lib):
@@ -98,6 +99,14 @@ def test_qkv_proj_validation(lib):
     assert qkvp(lib, kw=None) == EINVAL
     assert qkvp(lib, w=FAKE + 8) == EINVAL         # misaligned
     assert qkvp(lib, qkv=FAKE + 2) == EINVAL       # misaligned optional output
+    # small batches split the hidden dimension and need the workspace
+    need = lib.qil_qkv_proj_workspace_size(64, 32, 8, 4096)
+    assert need == 11 * 64 * 48 * 128 * 4            # 11 splits of fp32 partial sums
+    assert lib.qil_qkv_proj_workspace_size(2112, 32, 8, 4096) == 0
+    assert lib.qil_qkv_proj_workspace_size(64, 32, 8, 4000) == 0
+    assert qkvp(lib, T=64, work=None, workb=0) == EWS
+    assert qkvp(lib, T=64, workb=need - 1) == EWS
+    assert qkvp(lib, T=64, work=FAKE + 4) == EWS
 
 
 def dec(lib, **kw):
