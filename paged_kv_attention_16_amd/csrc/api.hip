@@ -427,13 +427,15 @@ namespace {
 // Split plan of the QKV projection (host integers only).  A workgroup holds
 // whole heads, so small batches give a grid of a few dozen workgroups, each
 // streaming a large slice of the weight; such batches split the hidden
-// dimension instead, aiming at ~256 workgroups, with at least four 64-column
-// slices per split and at most 16 splits.
+// dimension instead, into as many splits as fit one round of 256 workgroups
+// (one per CU: a split workgroup takes 144 KB of LDS; one workgroup more
+// would double the time), with at least four 64-column slices per split and
+// at most 16 splits.
 int32_t qkv_proj_splits(int32_t num_tokens, int32_t heads, int32_t hidden) {
   if (num_tokens <= 0 || num_tokens >= 1024) return 1;
   const int64_t blocks = (int64_t)(heads / 2) * ((num_tokens + 127) / 128);
   if (blocks >= 128) return 1;
-  int64_t s = (256 + blocks - 1) / blocks;
+  int64_t s = 256 / blocks;
   const int64_t smax = (int64_t)(hidden / 64) / 4;
   if (s > smax) s = smax;
   if (s > 16) s = 16;

@@ -552,10 +552,18 @@ hipError_t launch_qkv_proj(const QkvProjArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(qkv_proj_reduce_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  // 256-token workgroups from 1024 tokens on (measured on the Qwen3-8B
-  // shape: 2112 tokens run in one round of 216 workgroups instead of two
-  // rounds of 408); smaller batches keep more, smaller workgroups
-  if (a.num_tokens >= 1024) {
+  // One pass: pick the workgroup shape with the shorter estimated time,
+  // rounds of 256 CUs (one workgroup per CU) times the time of one round.
+  // Measured on the Qwen3-8B shape, a round of 128-token workgroups takes
+  // ~0.7 of a round of 256-token ones (they move more operand bytes per
+  // flop): 2112 tokens run in one round of 216 256-token workgroups rather
+  // than two of 408, while 1024 tokens run as one round of 192 128-token
+  // workgroups rather than 96 256-token ones.  256 tokens win when their
+  // estimate is no larger.
+  const int64_t pairs = heads / 2;
+  const int64_t rounds4 = (pairs * ((a.num_tokens + 255) / 256) + 255) / 256;
+  const int64_t rounds2 = (pairs * ((a.num_tokens + 127) / 128) + 255) / 256;
+  if (10 * rounds4 <= 7 * rounds2) {
     dim3 grid(heads / 2, (a.num_tokens + ProjCfg<4>::kTok - 1) / ProjCfg<4>::kTok);
     hipLaunchKernelGGL((qkv_proj_kernel<4, false>), grid, dim3(ProjCfg<4>::kThreads), 0, s, a);
   } else {

@@ -113,9 +113,10 @@ def small_case(seed, hidden, hq, hkv, ntok, page=16, drop=()):
     (128, 16, 8, 130, 8),    # two stages, a token stride above hidden
     (192, 32, 8, 129, 0),    # three stages, 8B head counts
     (1024, 40, 8, 200, 0),   # 14B head counts (28 head pairs), 0.6B hidden size
-    (1024, 16, 8, 1100, 0),  # 256-token workgroups (from 1024 tokens), ragged last tile
-    (4096, 32, 8, 64, 0),    # a decode step of the 8B shape: 11 splits of the hidden dimension
-    (4096, 32, 8, 16, 0),    # 16 tokens, 11 splits
+    (1024, 16, 8, 1100, 0),  # one round of 128-token workgroups, ragged last tile
+    (512, 32, 8, 1500, 0),   # 256-token workgroups (one round of 144), ragged last tile
+    (4096, 32, 8, 64, 0),    # a decode step of the 8B shape: 10 splits of the hidden dimension
+    (4096, 32, 8, 16, 0),    # 16 tokens, 10 splits
     (2048, 16, 8, 300, 8),   # 0.6B-like heads, 3 token tiles, split path with a token stride
 ])
 def test_small_shapes(qil, hidden, hq, hkv, ntok, x_pad):
