@@ -130,3 +130,33 @@ def test_debug_refuses_under_capture(debug):
         with pytest.raises(qil_mod.QilError) as ei:
             qil.paged_decode(out, q, c.kp, c.vp, c.bt, c.ctx, 40, float(w.scale))
     assert "capture" in str(ei.value)
+
+
+def test_qkv_proj_slots_and_positions(debug):
+    """The projection checks the same metadata as the fused write, before
+    either of its paths runs: slots in range and distinct, positions in
+    [0, max_position)."""
+    qil = debug
+    w, c = small_case()
+    T = int(c.new_slots.shape[0])
+    hq, hkv = w.num_q_heads, w.num_kv_heads
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    x = torch.randn(T, 256, device=DEV, generator=g).to(torch.bfloat16)
+    wt = (torch.randn((hq + 2 * hkv) * 128, 256, device=DEV, generator=g) / 16).to(torch.bfloat16)
+    q_out = torch.empty(T, hq, 128, dtype=torch.bfloat16, device=DEV)
+    wn = torch.ones(128, dtype=torch.bfloat16, device=DEV)
+    table = torch.zeros(64, 128, dtype=torch.float32, device=DEV)
+    pos = torch.arange(T, dtype=torch.int32, device=DEV)
+    run = lambda slots, p: qil.qkv_proj_write(x, wt, c.kp, c.vp, slots, q_out, hq, wn, wn, p, table)
+    bad = c.new_slots.clone()
+    bad[1] = w.num_pages * w.page_size
+    expect_einval(lambda: run(bad, pos), "slot_mapping[1]")
+    dup = c.new_slots.clone()
+    dup[6] = dup[2]
+    expect_einval(lambda: run(dup, pos), "are both")
+    badp = pos.clone()
+    badp[3] = 64                                # == max_position
+    expect_einval(lambda: run(c.new_slots, badp), "positions[3]")
+    run(c.new_slots, pos)                       # valid metadata runs
+    torch.cuda.synchronize()
