@@ -43,14 +43,14 @@ FLUSH_BYTES = 512 << 20
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--keys-per-split", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--mixed-layers", type=int, default=2,
+    ap.add_argument("--mixed-layers", type=int, default=36,
                     help="layers of the Qwen3-8B-shaped mixed step to time (36 in the full model)")
     ap.add_argument("--graph-layers", type=int, default=28,
                     help="layers of the decode step captured into a HIP graph per batch bucket "
@@ -109,6 +109,33 @@ def _pools(w, dev):
     shape = (w.num_pages, w.num_kv_heads, w.page_size, w.head_dim)
     raw = torch.full(shape, 0x7FC0, dtype=torch.int16, device=dev)
     return raw.view(torch.bfloat16), raw.clone().view(torch.bfloat16)
+
+
+class DeviceFilledInputs:
+    """A workload's inputs for timing only, drawn on the device: the same
+    metadata (lengths, block tables, slots, positions) as the workload, pools
+    and new rows N(0, 1) bf16 from a seeded device generator.  The 36 layers
+    of the mixed step (51 GB of pools) are filled in seconds this way; parity
+    runs use the host-drawn inputs."""
+
+    def __init__(self, w, dev, seed):
+        import torch
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        shape = (w.num_pages, w.num_kv_heads, w.page_size, w.head_dim)
+        self.kp = torch.randn(shape, generator=g, device=dev, dtype=torch.bfloat16)
+        self.vp = torch.randn(shape, generator=g, device=dev, dtype=torch.bfloat16)
+        t = int(w.new_lens.sum())
+        self.k_new = torch.randn((t, w.num_kv_heads, w.head_dim), generator=g, device=dev,
+                                 dtype=torch.bfloat16)
+        self.v_new = torch.randn((t, w.num_kv_heads, w.head_dim), generator=g, device=dev,
+                                 dtype=torch.bfloat16)
+        self.q = torch.randn((t, w.num_q_heads, w.head_dim), generator=g, device=dev,
+                             dtype=torch.bfloat16)
+        self.slots = _i32(w.slot_mapping_new(), dev)
+        self.bt = _i32(w.block_tables, dev)
+        self.ctx = _i32(w.context_lens, dev)
+        self.out = self.q.new_empty(self.q.shape)
 
 
 class Inputs:
@@ -285,7 +312,7 @@ def gpu_legs(args):
         t0 = time.time()
         for layer in range(args.mixed_layers):
             w5 = make_workload(5, layer)
-            x = Inputs(w5, dev)
+            x = DeviceFilledInputs(w5, dev, seed=5000 + layer)
             qw, kw = w5.norm_weights()
             x.table = torch.empty(w5.max_position, w5.head_dim, dtype=torch.float32, device=dev)
             qil.rope_cos_sin(x.table, w5.theta, stream=stream)
@@ -343,12 +370,16 @@ def gpu_legs(args):
         pre_flops5 = sum(w5.prefill_flops() for w5, _ in layers) / nl
         layer_ms = t["step_mean"] / nl
         res["mixed"] = dict(layers=nl, layer_ms=layer_ms, single_launch_layer_ms=t1["step_mean"] / nl,
+                            step_ms=t["step_mean"], step_ms_median=t["step_median"],
+                            step_ms_p10=t["step_p10"], step_ms_p90=t["step_p90"],
                             single_launch_ms=float(t1["mean"].reshape(nl, 2)[:, 1].mean()),
                             fused_ms=float(m[:, 0].mean()),
                             dec_ms=float(m[:, 1].mean()), pre_ms=float(m[:, 2].mean()),
                             fused_bytes=fused_bytes, dec_bytes=dec_bytes5, pre_flops=pre_flops5,
                             setup_s=mixed_setup)
-        print(f"[bench] mixed-8b x{nl} layers: {layer_ms*1e3:.1f} us/layer "
+        print(f"[bench] mixed-8b x{nl} layers: step {t['step_mean']*1e3:.1f} us (median "
+              f"{t['step_median']*1e3:.1f}, p10 {t['step_p10']*1e3:.1f}, p90 {t['step_p90']*1e3:.1f}), "
+              f"{layer_ms*1e3:.1f} us/layer "
               f"(fused write {m[:,0].mean()*1e3:.1f} us, decode {m[:,1].mean()*1e3:.1f} us, "
               f"prefill {m[:,2].mean()*1e3:.1f} us); decode + prefill in one launch: "
               f"{t1['step_mean'] / nl * 1e3:.1f} us/layer; setup {mixed_setup:.1f}s", flush=True)
@@ -725,7 +756,13 @@ def cpu_baseline(seconds):
     qbusy = time.perf_counter() - t0
     qflops = 2 * ntok * wb.shape[0] * 4096
     del kp5, vp5
-    return dict(value=nbytes / busy / 1e9, unit="GB/s", cores=cores, kind="oracle",
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((int(i.get("num_threads", 1)) for i in threadpool_info()
+                    if i.get("user_api") == "blas"), default=1)
+    except Exception:  # the count is informational
+        blas = None
+    return dict(value=nbytes / busy / 1e9, unit="GB/s", cores=cores, kind="oracle", blas_threads=blas,
                 sample=f"decode-b256 step, all {w.batch} requests (scatter write + fp64 decode over "
                        f"{nbytes / 1e6:.0f} MB of K/V), {busy:.1f} s on the host; "
                        f"{len(os.sched_getaffinity(0))} usable cores",
@@ -807,6 +844,8 @@ def main():
             "max_context": int(w.context_lens.max()),
             "page_size": int(w.page_size),
             "mall_flush": not args.no_flush,
+            "inputs": {"rng": "numpy PCG64, SeedSequence([1234, 3, 0, ...])",
+                       "metadata_sha256": w.metadata_digest()},
         },
         "roofline": {
             "bound": "hbm",
@@ -866,7 +905,11 @@ def main():
             "workload": "mixed-8b: Hq 32 / Hkv 8, per layer fused Q/K RMSNorm+RoPE write of 2112 "
                         "tokens, decode of 64 requests (context U[512,8192]), prefill of 4 x 512 "
                         "over prefixes U[0,4096]; page 16",
+            "inputs": "per layer the workload's own lengths, block tables, slots and positions; "
+                      "pools and new rows N(0,1) bf16 from a seeded device generator (timing only)",
             "layers_timed": m["layers"], "us_per_layer": round(m["layer_ms"] * 1e3, 1),
+            "step_us": {"mean": round(m["step_ms"] * 1e3, 1), "median": round(m["step_ms_median"] * 1e3, 1),
+                        "p10": round(m["step_ms_p10"] * 1e3, 1), "p90": round(m["step_ms_p90"] * 1e3, 1)},
             "us_per_layer_single_launch": round(m["single_launch_layer_ms"] * 1e3, 1),
             "single_launch_us": round(m["single_launch_ms"] * 1e3, 2),
             "us_per_36_layer_step": round(m["layer_ms"] * 1e3 * 36, 1),
