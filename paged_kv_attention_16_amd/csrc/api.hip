@@ -606,7 +606,6 @@ int qil_paged_attention_mixed(const qil_decode_batch* decode, const qil_prefill_
                      dtype, decode->keys_per_split, decode->workspace, decode->workspace_bytes, da,
                      &dec_empty);
     if (rc) return rc;
-    da.order = nullptr;  // the mixed grid deals out its decode splits itself
   }
   if (prefill) {
     rc = prep_prefill(prefill->out, prefill->q, k_cache, v_cache, prefill->block_tables,

@@ -342,18 +342,14 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(const int32
 
 template <int G, bool BF16>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
-  if (a.order != nullptr) {
-    hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderThreads), 0, s, a.context_lens,
-                       a.batch, a.max_context_len, a.order);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  hipError_t e = launch_decode_order(a, s);
+  if (e != hipSuccess) return e;
   dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
   if constexpr (BF16)
     hipLaunchKernelGGL((decode_mfma_kernel<G>), grid, dim3(64 * kMW), 0, s, a);
   else
     hipLaunchKernelGGL((decode_f32_kernel<G>), grid, dim3(64 * kFW), 0, s, a);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess || a.num_splits == 1) return e;
   hipLaunchKernelGGL((decode_merge_kernel<BF16>), dim3(a.num_q_heads, a.batch), dim3(128), 0, s, a);
   return hipGetLastError();
@@ -375,6 +371,13 @@ hipError_t launch_dtype(const DecodeArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_decode_order(const DecodeArgs& a, hipStream_t s) {
+  if (a.order == nullptr || a.batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderThreads), 0, s, a.context_lens,
+                     a.batch, a.max_context_len, a.order);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   return a.bf16 ? launch_dtype<true>(a, s) : launch_dtype<false>(a, s);

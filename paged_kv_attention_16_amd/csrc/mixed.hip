@@ -12,7 +12,9 @@
 // chunks of 8 of one kind, alternating while both kinds remain: workgroups
 // go to the 8 XCDs round robin, so each prefill block keeps its KV head's
 // XCD (KV head = block index mod 8 when num_kv_heads = 8), as in the
-// prefill-only launch.
+// prefill-only launch.  On large decode grids the decode blocks take their
+// requests longest first, through the order that qil_paged_decode's ordering
+// kernel writes.
 #include "decode_body.h"
 #include "prefill_body.h"
 
@@ -48,10 +50,13 @@ __global__ __launch_bounds__(kThreads) void mixed_kernel(PrefillArgs pa, int n_q
     prefill_tile<G>(pa, n_qtiles, g, rest % pa.batch, rest / pa.batch,
                     *reinterpret_cast<PrefillLds*>(lds));
   } else {
-    // the decode-only grid is (split, KV head, request), split fastest
+    // the decode-only grid is (split, KV head, request), split fastest;
+    // requests longest first when the order pass ran
     const int split = idx % da.num_splits;
     const int rest = idx / da.num_splits;
-    decode_mfma_split<G, kMixedWaves>(da, split, rest % da.num_kv_heads, rest / da.num_kv_heads,
+    const int zr = rest / da.num_kv_heads;
+    const int r = da.order != nullptr ? da.order[zr] : zr;
+    decode_mfma_split<G, kMixedWaves>(da, split, rest % da.num_kv_heads, r,
                                       reinterpret_cast<DecodeRing*>(lds));
   }
 }
@@ -65,6 +70,10 @@ hipError_t launch_g(const PrefillArgs& pa, const DecodeArgs& da, hipStream_t s) 
   const int64_t blocks = 8 * ((n_pre + 7) / 8 + (n_dec + 7) / 8);
   if (blocks == 0) return hipSuccess;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  if (n_dec > 0) {
+    hipError_t e = launch_decode_order(da, s);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((mixed_kernel<G>), dim3((unsigned)blocks), dim3(kThreads), 0, s, pa, n_qtiles,
                      (int)n_pre, da, (int)n_dec);
   hipError_t e = hipGetLastError();

@@ -100,6 +100,8 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// the request-order pass alone (when a.order is set), for launches that read it
+hipError_t launch_decode_order(const DecodeArgs& a, hipStream_t s);
 // the split merge alone (num_splits > 1), for launches that ran the splits
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s);
 
