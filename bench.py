@@ -38,6 +38,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 METRIC = "paged-decode attn GB/s (% of HBM peak) @B=256; prefill attn TFLOP/s (% MFMA)"
 FLUSH_BYTES = 512 << 20
+CUS, CLOCK_HZ = 256, 2.4e9     # MI355X compute units and peak engine clock
 
 
 def parse():
@@ -628,10 +629,24 @@ def measured_ceilings(dev, stream):
     t = timed_steps([mm], 3, 1, None, stream)
     flops = blocks * 4 * 4 * iters * 32768
     tf = flops / (t["step_mean"] * 1e-3) / 1e12
+    # LDS operand reads: bytes per clock per CU at the 2.4 GHz peak clock
+    lds = {}
+    lib.qil_ceiling_lds_read.argtypes = [i32, vp, i32, i32, vp]
+    for tr, name, per_lane in ((0, "ds_read_b128", 16), (1, "ds_read_b64_tr_b16", 8)):
+        lb, li = 1024, 2000
+
+        def lr():
+            rc = lib.qil_ceiling_lds_read(tr, ctypes.c_void_p(sink.data_ptr()), lb, li, s)
+            assert rc == 0, rc
+        t = timed_steps([lr], 3, 1, None, stream)
+        nb = lb * 512 * li * 16 * per_lane
+        lds[name] = round(nb / (t["step_mean"] * 1e-3) / CUS / CLOCK_HZ, 1)
     torch.cuda.empty_cache()
-    print(f"[bench] measured ceilings: stream read {best:.0f} GB/s, bf16 MFMA {tf:.0f} TFLOP/s",
-          flush=True)
-    return dict(stream_read_GB_s=round(best, 1), mfma_bf16_TFLOP_s=round(tf, 1))
+    print(f"[bench] measured ceilings: stream read {best:.0f} GB/s, bf16 MFMA {tf:.0f} TFLOP/s, "
+          f"LDS reads {lds['ds_read_b128']:.0f} B/clk/CU (b128), {lds['ds_read_b64_tr_b16']:.0f} "
+          f"(b64_tr_b16)", flush=True)
+    return dict(stream_read_GB_s=round(best, 1), mfma_bf16_TFLOP_s=round(tf, 1),
+                lds_read_B_per_clk_per_CU=lds)
 
 
 def graph_leg(args, dev, stream, flush):
@@ -890,6 +905,10 @@ def main():
             "traffic": traffic_for("prefill-varlen"),
             "measured_ceiling": res["ceilings"]["mfma_bf16_TFLOP_s"],
             "frac_of_measured": round(tf / res["ceilings"]["mfma_bf16_TFLOP_s"], 4),
+            # each wavefront reads a 64-key tile's K (16 x ds_read_b128) and V
+            # (32 x ds_read_b64_tr_b16) from LDS for its 32 query rows
+            "lds_reads_per_wave_tile": {"ds_read_b128": 16, "ds_read_b64_tr_b16": 32},
+            "lds_read_ceiling_B_per_clk_per_CU": res["ceilings"]["lds_read_B_per_clk_per_CU"],
         }
     if "prefill" in res:
         p = res["prefill"]
