@@ -178,3 +178,25 @@ def test_zero_tokens_is_a_no_op(qil):
     qil.qkv_proj_write(x, wt, kp, vp, e, q_out, 16, wn, wn, e, table)
     torch.cuda.synchronize()
     assert int(kp.abs().sum()) == 0
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_drawn_shapes(qil, case):
+    """Seeded draws of hidden size, head counts, token count, token stride and
+    dropped slots; the split path and both one-pass tile shapes all occur."""
+    rng = np.random.default_rng(9200 + case)
+    hidden = 64 * int(rng.integers(1, 41))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    hq = hkv * int(rng.choice([1, 2, 4, 5, 8]))
+    if hq % 2:
+        hq += hkv
+    ntok = int(rng.choice([1, 7, 64, 65, 128, 129, 255, 256, 257, int(rng.integers(1, 1500))]))
+    x_pad = int(rng.choice([0, 8, 64]))
+    ndrop = min(ntok - 1, int(rng.integers(0, 4)))
+    drop = tuple(int(i) for i in rng.choice(ntok, size=ndrop, replace=False)) if ndrop else ()
+    print(f"qkv_proj drawn {case}: hidden={hidden} hq={hq} hkv={hkv} tokens={ntok} "
+          f"pad={x_pad} dropped={drop}", flush=True)
+    x_bits, w_bits, npg, slots, pos, qw, kw, table = small_case(
+        700 + case, hidden, hq, hkv, max(ntok, 3), drop=drop)
+    x_bits, slots, pos = x_bits[:ntok], slots[:ntok], pos[:ntok]
+    check_case(qil, x_bits, w_bits, hq, hkv, 16, npg, slots, pos, qw, kw, 1e-6, table, x_pad)

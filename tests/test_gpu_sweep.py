@@ -1,0 +1,69 @@
+"""Seeded sweeps of qil_paged_prefill and qil_paged_decode over drawn shapes:
+GQA group size, KV heads, page size, batch, cached prefix and chunk lengths
+(edge values such as 1, the 64-key tile and page multiples drawn more often),
+each case against the fp64 oracle at the bf16 / fp32 tolerance.  The shapes
+are a fixed function of the case index, so every run checks the same cases."""
+
+import numpy as np
+import pytest
+import torch
+
+from tests import harness as H
+from workloads import make_custom
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+GROUPS = (1, 2, 4, 5, 8, 16)
+KV_HEADS = (1, 2, 4, 8)
+PAGES = (16, 32, 64, 128, 256)
+EDGES = (1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 257)
+
+
+def draw_len(rng, hi):
+    """A length in [1, hi]: an edge value a third of the time."""
+    if rng.random() < 1 / 3:
+        e = [v for v in EDGES if v <= hi]
+        return int(rng.choice(e))
+    return int(rng.integers(1, hi + 1))
+
+
+def draw_heads(rng):
+    g = int(rng.choice(GROUPS))
+    hkv = int(rng.choice(KV_HEADS))
+    while g * hkv > 64:
+        hkv //= 2
+    return g * hkv, hkv
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_prefill_sweep(qil, case):
+    rng = np.random.default_rng(9000 + case)
+    hq, hkv = draw_heads(rng)
+    page = int(rng.choice(PAGES))
+    batch = int(rng.integers(1, 6))
+    new = [draw_len(rng, 300) for _ in range(batch)]
+    prefix = [0 if rng.random() < 0.3 else draw_len(rng, 300) for _ in range(batch)]
+    ctx = [p + n for p, n in zip(prefix, new)]
+    print(f"prefill sweep {case}: hq={hq} hkv={hkv} page={page} new={new} ctx={ctx}", flush=True)
+    got, ref = H.run_small_prefill(DEV, ctx, new, hq, hkv, page, seed=500 + case)
+    print(f"  max abs err {np.max(np.abs(got - ref)):.3e}", flush=True)
+    assert H.excess(got, ref, "bf16") <= 0
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_decode_sweep(qil, case):
+    rng = np.random.default_rng(9100 + case)
+    hq, hkv = draw_heads(rng)
+    page = int(rng.choice(PAGES))
+    dtype = "f32" if case % 3 == 2 else "bf16"
+    batch = int(rng.integers(1, 41))
+    ctx = [draw_len(rng, 2000) for _ in range(batch)]
+    split = int(rng.choice([0, 64, 256]))
+    print(f"decode sweep {case}: {dtype} hq={hq} hkv={hkv} page={page} batch={batch} "
+          f"max ctx={max(ctx)} keys_per_split={split}", flush=True)
+    w = make_custom(ctx, [1] * batch, hq=hq, hkv=hkv, page=page, dtype=dtype, seed=600 + case,
+                    decode=True)
+    got, ref = H.run_decode_case(w, DEV, keys_per_split=split)
+    print(f"  max abs err {np.max(np.abs(got - ref)):.3e}", flush=True)
+    assert H.excess(got, ref, dtype) <= 0
