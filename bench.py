@@ -332,7 +332,13 @@ def gpu_legs(args):
             need = qil.paged_decode_workspace_size(64, w5.num_q_heads, w5.num_kv_heads, x.maxl_dec,
                                                    w5.page_size, 0)
             x.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            x.pre_need = qil.paged_prefill_workspace_size(len(w5.prefill_idx), int(x.q_pre.shape[0]),
+                                                          512, x.maxl_pre, w5.num_q_heads,
+                                                          w5.num_kv_heads, 0)
             layers.append((w5, x))
+        # one prefill workspace serves every layer: the calls run in order on one stream
+        pre_ws = torch.empty(max(max(x.pre_need for _, x in layers), 1), dtype=torch.uint8,
+                             device=dev)
         torch.cuda.synchronize()
         mixed_setup = time.time() - t0
         segs = []
@@ -346,11 +352,12 @@ def gpu_legs(args):
 
             def pre(x=x, w5=w5):
                 qil.paged_prefill(x.out_pre, x.q_pre, x.kp, x.vp, x.bt_pre, x.cu_pre, x.ctx_pre,
-                                  512, x.maxl_pre, float(w5.scale), stream=stream)
+                                  512, x.maxl_pre, float(w5.scale), workspace=pre_ws, stream=stream)
             segs += [fused, dec, pre]
         t = timed_steps(segs, args.steps, args.warmup, flush, stream)
         nl = len(layers)
         m = t["mean"].reshape(nl, 3)
+
         # the same layers with decode and prefill in one launch per layer
         segs1 = []
         for i, (w5, x) in enumerate(layers):
@@ -376,6 +383,7 @@ def gpu_legs(args):
                             single_launch_ms=float(t1["mean"].reshape(nl, 2)[:, 1].mean()),
                             fused_ms=float(m[:, 0].mean()),
                             dec_ms=float(m[:, 1].mean()), pre_ms=float(m[:, 2].mean()),
+
                             fused_bytes=fused_bytes, dec_bytes=dec_bytes5, pre_flops=pre_flops5,
                             setup_s=mixed_setup)
         print(f"[bench] mixed-8b x{nl} layers: step {t['step_mean']*1e3:.1f} us (median "
@@ -391,6 +399,8 @@ def gpu_legs(args):
     if not args.skip_shared:
         res["shared"] = shared_prefix_leg(args, dev, stream, flush)
     res["shard"] = shard_leg(args, dev, stream, flush)
+    if not args.skip_prefill:
+        res["long_prefix"] = long_prefix_leg(args, dev, stream, flush)
     if not args.skip_qkv_proj:
         res["qkv_proj"] = qkv_proj_leg(args, dev, stream, flush)
     return res
@@ -478,6 +488,48 @@ def shared_prefix_leg(args, dev, stream, flush):
 
 
 GRAPH_BUCKETS = (1, 2, 4, 8, 16, 32, 64, 128, 256)
+
+
+def long_prefix_leg(args, dev, stream, flush):
+    """Chunked prefill of a long prompt: one 512-token chunk after a cached
+    prefix of 7,680 / 15,872 / 32,256 tokens (contexts 8k / 16k / 32k),
+    Qwen3-8B attention (Hq 32 / Hkv 8), page 16.  Only 64 query tiles x KV
+    heads, so whole tiles leave most CUs idle; the automatic plan splits each
+    tile over its keys.  Timing only (N(0,1) bf16 pools, random placement);
+    parity is a GPU test."""
+    import torch
+    import paged_kv_attention_16_amd as qil
+    rng = np.random.default_rng(17)
+    hq, hkv, page, D, n = 32, 8, 16, 128, 512
+    scale = 0.08838834764831845
+    out = []
+    for L in (8192, 16384, 32768):
+        pages = L // page
+        num_pages = int(pages * 1.2)
+        bt = torch.from_numpy(rng.permutation(num_pages)[:pages].astype(np.int32)[None]).to(dev)
+        kp = torch.empty(num_pages, hkv, page, D, dtype=torch.bfloat16, device=dev).normal_()
+        vp = torch.empty_like(kp).normal_()
+        q = torch.randn(n, hq, D, device=dev).to(torch.bfloat16)
+        o = torch.empty_like(q)
+        cu = torch.tensor([0, n], dtype=torch.int32, device=dev)
+        ctx = torch.tensor([L], dtype=torch.int32, device=dev)
+        need = qil.paged_prefill_workspace_size(1, n, n, L, hq, hkv, 0)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        flops = sum(L - n + i + 1 for i in range(n)) * hq * 512
+        row = dict(workload=f"one {n}-token chunk over a {L - n}-token prefix", context=L)
+        for label, kps in (("split", 0), ("unsplit", L)):
+            ms = flushed_kernel_ms(lambda: qil.paged_prefill(o, q, kp, vp, bt, cu, ctx, n, L, scale,
+                                                             keys_per_split=kps, workspace=ws,
+                                                             stream=stream), args, flush, stream)
+            tf = flops / (ms * 1e-3) / 1e12
+            row[label] = dict(us=round(ms * 1e3, 2), TFLOP_per_s=round(tf, 1),
+                              frac=round(tf / BF16_PEAK_TFLOPS, 4))
+        out.append(row)
+        print(f"[bench] long prefix L={L}: split {row['split']['us']} us "
+              f"({row['split']['TFLOP_per_s']} TFLOP/s), unsplit {row['unsplit']['us']} us", flush=True)
+        del kp, vp
+    torch.cuda.empty_cache()
+    return out
 
 
 def shard_leg(args, dev, stream, flush):
@@ -970,6 +1022,12 @@ def main():
                 "library_gemm_then_fused_write": round(qp["decode_step_library_ms"] * 1e3, 2)}}
     if "shard" in res:
         line["tp8_shard_decode"] = res["shard"]
+    if "long_prefix" in res:
+        line["prefill_long_prefix"] = {
+            "workload": "chunked prefill of a long prompt: Hq 32 / Hkv 8, page 16, one 512-token "
+                        "chunk after a cached prefix; query tiles split over keys (automatic plan) "
+                        "vs run whole",
+            "cases": res["long_prefix"]}
     if not args.skip_cpu:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -265,15 +265,36 @@ int qil_paged_decode(void* out, const void* q, const void* k_cache, const void* 
  *                  (n_r <= context_lens[r]); new token i sits at position
  *                  context_lens[r] - n_r + i
  *   max_seqlen_q   host int >= every n_r;  max_context_len host int >= every context_lens[r]
+ *   keys_per_split 0 = automatic, else a multiple of 64 up to 65472: a query
+ *                  tile (256/G new tokens x the G query heads of one KV head)
+ *                  whose visible keys span more than this many is cut into
+ *                  pieces of near-equal length (at most 32 pieces: a smaller
+ *                  value is raised to fit), each run by its own workgroup, and
+ *                  the pieces are merged by the log-sum-exp rule.  Automatic
+ *                  splitting applies when the call has fewer than 160 query
+ *                  tiles x KV heads and max_context_len is at least 2,048, e.g.
+ *                  a chunk of a long prompt.  Splitting needs
+ *                  batch * ceil(max_seqlen_q / (256/G)) <= 4096; larger calls
+ *                  run unsplit whatever keys_per_split says.
+ *   workspace      device scratch of at least qil_paged_prefill_workspace_size(...)
+ *                  bytes (may be NULL when that size is 0); its contents on
+ *                  entry do not matter.  It holds the list of pieces, ordered
+ *                  longest first by a small planning kernel, and the pieces'
+ *                  partial rows.  Results do not depend on that order.
  * The K/V rows of the new tokens must already be in the pools (qil_kv_write
  * first).  Requests with n_r == 0 and batch == 0 are no-ops.
  */
+size_t qil_paged_prefill_workspace_size(int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                                        int32_t max_context_len, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t keys_per_split);
+
 int qil_paged_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, int32_t block_table_stride,
                       const int32_t* cu_seqlens_q, const int32_t* context_lens, int32_t batch,
                       int32_t total_q, int32_t max_seqlen_q, int32_t max_context_len,
                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                       int32_t page_size, int32_t num_pages, float scale, int32_t dtype,
+                      int32_t keys_per_split, void* workspace, size_t workspace_bytes,
                       void* stream);
 
 /*
@@ -290,7 +311,7 @@ int qil_paged_prefill(void* out, const void* q, const void* k_cache, const void*
  *            qil_paged_decode_workspace_size (same split plan)
  *   prefill  NULL or a prefill batch (its K/V rows already written)
  * Both batches use k_cache / v_cache, the head counts, page size, scale and
- * dtype given here.  Each batch's arguments are checked as in its own call
+ * dtype given here.  The prefill part runs whole query tiles (unsplit).  Each batch's arguments are checked as in its own call
  * (a NULL or empty batch is allowed); outputs must not overlap.
  */
 typedef struct qil_decode_batch {

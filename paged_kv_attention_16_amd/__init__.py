@@ -3,7 +3,7 @@
 Argument marshalling only: every step of the path runs in the HIP kernels of
 libqil.so (built in-tree by ``paged_kv_attention_16_amd.build``).  torch is
 used for device memory (``data_ptr()``), the current stream, and -- when the
-caller passes none -- the decode workspace allocation.  There is no CPU
+caller passes none -- the decode and prefill workspace allocations.  There is no CPU
 fallback: if the library is missing or fails to load, every call raises.
 
 The functions mirror the C ABI in include/qil.h:
@@ -21,7 +21,8 @@ import os
 
 __all__ = [
     "QilError", "lib_path", "load", "version", "kv_write", "QKNormRope", "rope_cos_sin",
-    "paged_decode", "paged_decode_workspace_size", "paged_prefill", "paged_attention_mixed",
+    "paged_decode", "paged_decode_workspace_size", "paged_prefill", "paged_prefill_workspace_size",
+    "paged_attention_mixed",
     "qkv_proj_write", "qkv_proj_workspace_size", "set_debug", "debug_enabled",
     "QIL_F32", "QIL_BF16",
 ]
@@ -113,7 +114,9 @@ def load(path=None):
                                               i32, i32, i32, f32, i32, vp]
     lib.qil_paged_prefill.restype = ctypes.c_int
     lib.qil_paged_prefill.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
-                                      i32, i32, i32, i32, f32, i32, vp]
+                                      i32, i32, i32, i32, f32, i32, i32, vp, sz, vp]
+    lib.qil_paged_prefill_workspace_size.restype = sz
+    lib.qil_paged_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     if path is None:
         _LIB = lib
     return lib
@@ -270,17 +273,31 @@ def paged_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_conte
     _check(rc)
 
 
+def paged_prefill_workspace_size(batch, total_q, max_seqlen_q, max_context_len, num_q_heads,
+                                 num_kv_heads, keys_per_split=0):
+    return int(load().qil_paged_prefill_workspace_size(batch, total_q, max_seqlen_q,
+                                                       max_context_len, num_q_heads, num_kv_heads,
+                                                       keys_per_split))
+
+
 def paged_prefill(out, q, k_cache, v_cache, block_tables, cu_seqlens_q, context_lens,
-                  max_seqlen_q, max_context_len, scale, stream=None):
+                  max_seqlen_q, max_context_len, scale, keys_per_split=0, workspace=None,
+                  stream=None):
     """out, q: [total_q, Hq, 128] bf16 packed by cu_seqlens_q (int32 [B+1])."""
+    import torch
     num_pages, hkv, page, d = _pool_shape(k_cache)
     total_q, hq = int(q.shape[0]), int(q.shape[1])
     batch = int(context_lens.shape[0])
+    need = paged_prefill_workspace_size(batch, total_q, int(max_seqlen_q), int(max_context_len),
+                                        hq, hkv, keys_per_split)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = load().qil_paged_prefill(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         int(block_tables.shape[1]), _ptr(cu_seqlens_q), _ptr(context_lens), batch, total_q,
         int(max_seqlen_q), int(max_context_len), hq, hkv, d, page, num_pages, float(scale),
-        _dtype_code(q), _stream(stream))
+        _dtype_code(q), int(keys_per_split), _ptr(workspace), ws_bytes, _stream(stream))
     _check(rc)
 
 

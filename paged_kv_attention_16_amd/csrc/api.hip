@@ -10,6 +10,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include <hip/hip_runtime.h>
@@ -299,6 +300,94 @@ int prep_decode(void* out, const void* q, const void* k_cache, const void* v_cac
   return QIL_OK;
 }
 
+// Split plan of a prefill call (host integers only).  The grid of whole
+// query tiles has one workgroup per CU at a time (8 waves of 205 registers);
+// when it holds fewer than 160 tiles with rows, one round of long tiles sets
+// the time while most CUs idle.  Such calls cut every query tile into pieces
+// of at most S 64-key tiles, S chosen for one piece per CU if every tile were
+// as long as the longest possible one, and at least 16 key tiles.  Each
+// piece loads its queries and writes a partial row block, and the split adds
+// a planning and a merge launch, so shorter pieces or busier grids cost more
+// than they balance (measured on one chunk over a long prefix, and on the
+// 8B mixed step's 256 tiles, where whole tiles stay faster).
+struct PrefillPlan {
+  int32_t S = 0;            // 0: unsplit
+  int32_t pieces = 1;       // pieces of the longest possible tile
+  int32_t n_qtiles = 0;
+  int32_t entries = 0;      // bound on query tiles with rows
+  int64_t items = 0;        // bound on pieces
+};
+
+constexpr int32_t kMaxPrefillKeysPerSplit = 64 * 1023;
+constexpr int32_t kAutoSplitTiles = 160;   // auto-split below this many query tiles x KV heads
+constexpr int32_t kMinPieceTiles = 16;
+
+PrefillPlan plan_prefill(int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                         int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t keys_per_split) {
+  PrefillPlan p;
+  if (batch <= 0 || total_q <= 0 || max_seqlen_q <= 0 || max_context_len <= 0 ||
+      num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads)
+    return p;
+  const int32_t tq = 256 / (num_q_heads / num_kv_heads);
+  if (tq <= 0) return p;
+  const int64_t n_qtiles = (max_seqlen_q + tq - 1) / tq;
+  const int64_t all = (int64_t)batch * n_qtiles;
+  if (all > qil::kMaxPlanEntries) return p;
+  const int64_t entries = std::min<int64_t>(all, (total_q + tq - 1) / tq + batch);
+  const int64_t kt_max = (max_context_len + 63) / 64;
+  int64_t S;
+  if (keys_per_split > 0) {
+    S = keys_per_split / 64;
+  } else {
+    const int64_t tiles = entries * num_kv_heads;
+    if (tiles >= kAutoSplitTiles || kt_max < 2 * kMinPieceTiles) return p;
+    S = std::max<int64_t>(kMinPieceTiles, (kt_max * tiles + 255) / 256);
+  }
+  S = std::min<int64_t>(S, qil::kMaxPieceTiles);
+  if ((kt_max + S - 1) / S > qil::kMaxPieces) S = (kt_max + qil::kMaxPieces - 1) / qil::kMaxPieces;
+  const int64_t pieces = (kt_max + S - 1) / S;
+  if (pieces <= 1 || entries * pieces * num_kv_heads > INT32_MAX) return p;
+  p.S = (int32_t)S;
+  p.pieces = (int32_t)pieces;
+  p.n_qtiles = (int32_t)n_qtiles;
+  p.entries = (int32_t)entries;
+  p.items = entries * pieces;
+  return p;
+}
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace of a split prefill: header, piece list, split list, then the
+// partial rows (bf16) and their (max, sum) pairs.
+size_t prefill_workspace_bytes(const PrefillPlan& p, int32_t num_kv_heads) {
+  if (p.S == 0) return 0;
+  const size_t slabs = (size_t)p.entries * p.pieces * num_kv_heads;
+  return 256 + round256((size_t)p.items * 32) + round256((size_t)p.entries * 16) +
+         round256(slabs * 256 * 128 * 2) + slabs * 256 * 2 * 4;
+}
+
+qil::PrefillSplit prefill_split_args(const PrefillPlan& p, int32_t num_kv_heads, void* ws) {
+  char* b = static_cast<char*>(ws);
+  const size_t slabs = (size_t)p.entries * p.pieces * num_kv_heads;
+  qil::PrefillSplit sp;
+  sp.tiles_per_piece = p.S;
+  sp.max_pieces = p.pieces;
+  sp.n_qtiles = p.n_qtiles;
+  sp.max_entries = p.entries;
+  sp.max_items = (int32_t)p.items;
+  sp.header = reinterpret_cast<int32_t*>(b);
+  b += 256;
+  sp.items = reinterpret_cast<int32_t*>(b);
+  b += round256((size_t)p.items * 32);
+  sp.splits = reinterpret_cast<int32_t*>(b);
+  b += round256((size_t)p.entries * 16);
+  sp.part_o = reinterpret_cast<uint16_t*>(b);
+  b += round256(slabs * 256 * 128 * 2);
+  sp.part_ml = reinterpret_cast<float*>(b);
+  return sp;
+}
+
 // Validate a prefill call and fill its launch arguments.  *empty is set when
 // the call has nothing to do.
 int prep_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -567,25 +656,46 @@ int qil_paged_decode(void* out, const void* q, const void* k_cache, const void* 
   return ok();
 }
 
+size_t qil_paged_prefill_workspace_size(int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                                        int32_t max_context_len, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t keys_per_split) {
+  if (keys_per_split < 0 || keys_per_split % 64 || keys_per_split > kMaxPrefillKeysPerSplit)
+    return 0;
+  return prefill_workspace_bytes(plan_prefill(batch, total_q, max_seqlen_q, max_context_len,
+                                              num_q_heads, num_kv_heads, keys_per_split),
+                                 num_kv_heads);
+}
+
 int qil_paged_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, int32_t block_table_stride,
                       const int32_t* cu_seqlens_q, const int32_t* context_lens, int32_t batch,
                       int32_t total_q, int32_t max_seqlen_q, int32_t max_context_len,
                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                       int32_t page_size, int32_t num_pages, float scale, int32_t dtype,
+                      int32_t keys_per_split, void* workspace, size_t workspace_bytes,
                       void* stream) {
   qil::PrefillArgs a;
   bool empty = false;
+  if (keys_per_split < 0 || keys_per_split % 64 || keys_per_split > kMaxPrefillKeysPerSplit)
+    return fail(QIL_EINVAL, "keys_per_split %d must be 0 or a multiple of 64 up to %d",
+                keys_per_split, kMaxPrefillKeysPerSplit);
   int rc = prep_prefill(out, q, k_cache, v_cache, block_tables, block_table_stride, cu_seqlens_q,
                         context_lens, batch, total_q, max_seqlen_q, max_context_len, num_q_heads,
                         num_kv_heads, head_dim, page_size, num_pages, scale, dtype, a, &empty);
   if (rc || empty) return rc;
+  const PrefillPlan plan = plan_prefill(batch, total_q, max_seqlen_q, max_context_len,
+                                        num_q_heads, num_kv_heads, keys_per_split);
+  const size_t need = prefill_workspace_bytes(plan, num_kv_heads);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(QIL_EWORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (debug_on()) {
     rc = run_checks(s, [&](qil::DebugReport* rep) { return check_prefill_metadata(a, rep, s); });
     if (rc) return rc;
   }
-  hipError_t e = qil::launch_prefill(a, s);
+  hipError_t e = need > 0 ? qil::launch_prefill_split(a, prefill_split_args(plan, num_kv_heads, workspace), s)
+                          : qil::launch_prefill(a, s);
   if (e != hipSuccess) return fail(QIL_EHIP, "prefill launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -89,14 +89,18 @@ constexpr int kRowsPerWave = kBN / kWaves;  // tile rows each wavefront loads
 // LDS of one workgroup: [slot][K | V][64 rows x 256 bytes].
 typedef char PrefillLds[2][2][kBN * 256];
 
-// One query tile: KV head g, request r, tile index z counted from the last
-// tile (z = 0 is the tile with the most keys).  Every thread of the
-// kThreads-thread workgroup calls it; `smem` is the workgroup's LDS.
+// Key tiles [kt_begin, kt_end) of one query tile: KV head g, request r,
+// query tile `tile`.  With part_o null the rows are final and go to a.out;
+// otherwise this is one piece of a split tile, and each row's output
+// normalized by its own sum goes to part_o (bf16, [256 rows][128]) with the
+// row's reference maximum (log2 domain) and sum to part_ml (rows
+// ml_row_stride pairs apart).  Every thread
+// of the kThreads-thread workgroup calls it; `smem` is the workgroup's LDS.
 template <int G>
-__device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int n_qtiles, int g, int r,
-                                             int z, PrefillLds& smem) {
+__device__ __forceinline__ void prefill_range(const PrefillArgs& a, int g, int r, int tile,
+                                              int kt_begin, int kt_end, uint16_t* part_o,
+                                              float* part_ml, int ml_row_stride, PrefillLds& smem) {
   constexpr int TQ = kRowsWG / G;  // tokens per workgroup
-  const int tile = n_qtiles - 1 - z;
   const int q0 = a.cu_seqlens[r];
   // rows of this request, kept inside [0, total_q)
   const int n = min(a.cu_seqlens[r + 1], a.total_q) - max(q0, 0);
@@ -106,7 +110,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int n_qtiles,
   const int prefix = L - n;
   const int tvalid = min(TQ, n - t0);
   const int kmax = prefix + t0 + tvalid;  // keys [0, kmax) are visible to some row
-  const int ntiles = kmax > 0 ? (kmax + kBN - 1) / kBN : 0;
+  const int ntiles = min(kmax > 0 ? (kmax + kBN - 1) / kBN : 0, kt_end);
+  const int kt0 = kt_begin;
   const int pos_min = prefix + t0;
 
   const int tid = threadIdx.x;
@@ -319,10 +324,12 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int n_qtiles,
   };
 
   // Tiles [0, nfree) lie wholly at or before the first token's position and
-  // need no mask; the rest (the diagonal band) are masked.
+  // need no mask; the rest (the diagonal band) are masked.  Page ids are
+  // fetched 64 tiles at a time from a multiple of 64, so lane i always holds
+  // the page of tile (kt & ~63) + i.
   const int nfree = min(ntiles, (pos_min + 1) / kBN);
   auto tile_step = [&](auto mask_tag, int kt) __attribute__((always_inline)) {
-    const int buf = kt & 1;
+    const int buf = (kt - kt0) & 1;
     if (kt + 1 < ntiles) {
       if (((kt + 1) & 63) == 0) fetch_pages(kt + 1);
       issue_tile(kt + 1, buf ^ 1);
@@ -331,21 +338,27 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int n_qtiles,
     __builtin_amdgcn_s_waitcnt(0);  // this wavefront's loads of the next tile have landed
     __syncthreads();
   };
-  if (ntiles > 0) {
-    fetch_pages(0);
+  if (kt0 < ntiles) {
+    fetch_pages(kt0 & ~63);
     __syncthreads();  // the zero fill is complete before any load lands
-    issue_tile(0, 0);
+    issue_tile(kt0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int kt = 0; kt < nfree; ++kt) tile_step(std::false_type{}, kt);
-    for (int kt = nfree; kt < ntiles; ++kt) tile_step(std::true_type{}, kt);
+    for (int kt = kt0; kt < nfree; ++kt) tile_step(std::false_type{}, kt);
+    for (int kt = max(nfree, kt0); kt < ntiles; ++kt) tile_step(std::true_type{}, kt);
   }
 
   const float ltot = sum_halves(lrun);
   if (!row_valid) return;
   const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
-  uint16_t* orow =
-      static_cast<uint16_t*>(a.out) + ((int64_t)(q0 + t0 + tok) * Hq + g * G + hh) * kHeadDim;
+  uint16_t* orow;
+  if (part_o) {
+    // one piece of a split tile: this row's normalized output and (m, l)
+    orow = part_o + rho * kHeadDim;
+    if (hf == 0) *reinterpret_cast<float2*>(part_ml + 2 * rho * ml_row_stride) = make_float2(mref, ltot);
+  } else {
+    orow = static_cast<uint16_t*>(a.out) + ((int64_t)(q0 + t0 + tok) * Hq + g * G + hh) * kHeadDim;
+  }
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -357,6 +370,14 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int n_qtiles,
       *reinterpret_cast<uint2*>(orow + d0) = st;
     }
   }
+}
+
+// One whole query tile, z counted from the last tile (z = 0 is the tile with
+// the most keys).
+template <int G>
+__device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int n_qtiles, int g, int r,
+                                             int z, PrefillLds& smem) {
+  prefill_range<G>(a, g, r, n_qtiles - 1 - z, 0, 1 << 30, nullptr, nullptr, 0, smem);
 }
 
 template <int G>

@@ -126,7 +126,31 @@ struct PrefillArgs {
   float scale;
 };
 
+// Split plan of a prefill call.  A query tile whose key range spans more
+// than tiles_per_piece 64-key tiles is cut into pieces of near-equal length,
+// each run by its own workgroup; a planning kernel orders all pieces longest
+// first, and a merge kernel combines the pieces of each split tile.  The
+// pointers lie in the caller's workspace.
+struct PrefillSplit {
+  int32_t tiles_per_piece;  // S >= 1 (<= kMaxPieceTiles)
+  int32_t max_pieces;       // pieces of the longest possible tile, <= kMaxPieces
+  int32_t n_qtiles;         // query tiles of the longest request
+  int32_t max_entries;      // bound on query tiles with rows (split entries too)
+  int32_t max_items;        // bound on pieces: max_entries * max_pieces
+  int32_t* header;          // [0] pieces planned, [1] split tiles
+  int32_t* items;           // [max_items][8]: r, tile, kt_begin, kt_end, piece, pieces, split slot, 0
+  int32_t* splits;          // [max_entries][4]: r, tile, pieces, 0
+  uint16_t* part_o;         // [max_entries][max_pieces][Hkv][256 rows][128] bf16, normalized
+  float* part_ml;           // [max_entries][Hkv][256 rows][max_pieces][2]: reference max (log2), sum
+};
+
+constexpr int kMaxPieceTiles = 1023;   // planner bins: piece lengths 1 .. 1023 tiles
+constexpr int kMaxPieces = 32;         // pieces per query tile
+constexpr int kMaxPlanEntries = 4096;  // batch * n_qtiles of a split call
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+// plan, pieces and merge of a split call
+hipError_t launch_prefill_split(const PrefillArgs& a, const PrefillSplit& sp, hipStream_t s);
 
 // ---- single-launch mixed batch (bf16): prefill tiles and decode splits ----
 // in one grid, then the decode merge when the decode part has several splits

@@ -103,7 +103,7 @@ class DeviceCase:
                          float(w.scale), keys_per_split=keys_per_split)
         return out
 
-    def prefill(self, requests=None, out=None):
+    def prefill(self, requests=None, out=None, keys_per_split=0):
         w = self.w
         reqs = np.asarray(w.prefill_idx if requests is None else requests)
         rows = torch.from_numpy(self.rows_of(reqs)).to(self.dev)
@@ -114,7 +114,8 @@ class DeviceCase:
         cu = i32(w.cu_seqlens(reqs), self.dev)
         out = torch.empty_like(q) if out is None else out
         qil.paged_prefill(out, q, self.kp, self.vp, bt, cu, ctx, int(w.new_lens[reqs].max()),
-                          int(w.context_lens[reqs].max()), float(w.scale))
+                          int(w.context_lens[reqs].max()), float(w.scale),
+                          keys_per_split=keys_per_split)
         return out
 
 

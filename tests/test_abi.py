@@ -145,11 +145,13 @@ def test_decode_validation(lib):
 
 def pre(lib, **kw):
     a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, bts=200, cu=FAKE, ctx=FAKE, B=8, T=8000,
-             maxq=2048, maxL=2560, hq=16, hkv=8, d=128, page=16, pages=900, scale=0.088, dtype=1)
+             maxq=2048, maxL=2560, hq=16, hkv=8, d=128, page=16, pages=900, scale=0.088, dtype=1,
+             kps=0, ws=None, wsb=0)
     a.update(kw)
     return lib.qil_paged_prefill(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["bts"], a["cu"],
                                  a["ctx"], a["B"], a["T"], a["maxq"], a["maxL"], a["hq"], a["hkv"],
-                                 a["d"], a["page"], a["pages"], a["scale"], a["dtype"], None)
+                                 a["d"], a["page"], a["pages"], a["scale"], a["dtype"], a["kps"],
+                                 a["ws"], a["wsb"], None)
 
 
 def test_prefill_validation(lib):
@@ -163,6 +165,34 @@ def test_prefill_validation(lib):
     assert pre(lib, hq=16, hkv=3) == EINVAL
     assert pre(lib, page=512) == EUNSUP
     assert pre(lib, B=-1) == EINVAL
+    assert pre(lib, kps=100) == EINVAL              # not a multiple of 64
+    assert pre(lib, kps=-64) == EINVAL
+    assert pre(lib, kps=64 * 1024) == EINVAL        # above 65472
+
+
+def test_prefill_split_workspace(lib):
+    ws = lib.qil_paged_prefill_workspace_size
+    # 8 chunks of up to 2,048 tokens: 568 query tiles x KV heads, never split automatically
+    assert ws(8, 8000, 2048, 2560, 16, 8, 0) == 0
+    # an explicit split of the same call needs a workspace; longer pieces need no more
+    s1024 = ws(8, 8000, 2048, 2560, 16, 8, 1024)
+    assert s1024 > 0 and ws(8, 8000, 2048, 2560, 16, 8, 2048) <= s1024
+    assert ws(8, 8000, 2048, 2560, 16, 8, 4096) == 0    # every tile fits one piece
+    # one 512-token chunk over an 8k context (Hq 32 / Hkv 8): 64 tiles, split automatically
+    auto = ws(1, 512, 512, 8192, 32, 8, 0)
+    assert auto > 0
+    # at most 32 pieces per tile: a tiny keys_per_split is raised, so the size is bounded
+    assert ws(1, 512, 512, 8192, 32, 8, 64) == ws(1, 512, 512, 8192, 32, 8, 256)
+    # more than 4,096 query tiles in the plan: unsplit
+    assert ws(5000, 5000, 1, 4096, 16, 8, 1024) == 0
+    assert ws(1, 512, 512, 8192, 32, 8, 100) == 0       # invalid keys_per_split
+    # calls that need a workspace reject a missing, short or misaligned one
+    kw = dict(B=1, T=512, maxq=512, maxL=8192, hq=32, hkv=8, bts=512)
+    assert pre(lib, **kw) == EWS
+    assert pre(lib, ws=FAKE, wsb=auto - 1, **kw) == EWS
+    assert pre(lib, ws=FAKE + 4, wsb=auto, **kw) == EWS
+    assert pre(lib, kps=4096, **kw) == EWS             # two explicit 4k-key pieces
+    assert ws(1, 512, 512, 8192, 32, 8, 8192) == 0       # one piece covers every tile
 
 
 def test_rope_table_validation(lib):

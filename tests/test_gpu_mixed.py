@@ -41,10 +41,13 @@ def separate(qil, w, case, dec, pre):
         qil.paged_decode(out_d, dec["q"], case.kp, case.vp, dec["block_tables"], dec["context_lens"],
                          dec["max_context_len"], float(w.scale))
     if pre is not None:
+        # the single launch runs whole query tiles: so does this call (one
+        # piece spans every context), which makes the two bitwise comparable
         out_p = torch.empty_like(pre["q"])
+        whole = (pre["max_context_len"] + 63) // 64 * 64
         qil.paged_prefill(out_p, pre["q"], case.kp, case.vp, pre["block_tables"], pre["cu_seqlens_q"],
                           pre["context_lens"], pre["max_seqlen_q"], pre["max_context_len"],
-                          float(w.scale))
+                          float(w.scale), keys_per_split=whole)
     torch.cuda.synchronize()
     return out_d, out_p
 

@@ -1,0 +1,148 @@
+"""qil_paged_prefill with query tiles split over their keys (pieces ordered
+longest first, merged by the log-sum-exp rule) against the oracle: forced
+splits over ragged varlen batches and every GQA group size, the automatic
+split of a chunk over a long prefix, the 8B-shaped mixed step's prefill
+split on request, the bit-exact indexing probe, page-permutation invariance and
+run-twice determinism."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_attention_16_amd as qil
+from tests import harness as H
+from workloads import bf16_from_f32, make_custom, make_workload
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def auto_splits(w, reqs):
+    return qil.paged_prefill_workspace_size(len(reqs), int(w.new_lens[reqs].sum()),
+                                            int(w.new_lens[reqs].max()),
+                                            int(w.context_lens[reqs].max()), w.num_q_heads,
+                                            w.num_kv_heads, 0) > 0
+
+
+@pytest.mark.parametrize("hq,hkv,kps", [(16, 8, 128), (16, 8, 512), (32, 8, 256), (8, 8, 64),
+                                        (64, 4, 192), (40, 8, 320), (128, 8, 64)])
+def test_forced_split_ragged(qil, hq, hkv, kps):
+    # chunks straddle query and key tiles; prefixes make several pieces per tile
+    ctx = [1, 700, 1300, 90, 2100, 333]
+    new = [1, 300, 257, 90, 40, 1]
+    w = make_custom(ctx, new, hq=hq, hkv=hkv, page=16, seed=hq + kps)
+    case = H.DeviceCase(w, DEV)
+    print(f"forced split hq={hq} hkv={hkv} keys_per_split={kps}", flush=True)
+    split = H.to_f64(case.prefill(keys_per_split=kps))
+    whole = H.to_f64(case.prefill())
+    ref = H.OracleCase(w, case.data, range(w.batch)).attention(range(w.batch))
+    print("  max abs err split", np.max(np.abs(split - ref)), "unsplit", np.max(np.abs(whole - ref)),
+          flush=True)
+    assert H.excess(split, ref, "bf16") <= 0
+    assert np.max(np.abs(split - whole)) < 2e-2
+
+
+@pytest.mark.parametrize("page", [16, 256])
+def test_auto_split_long_prefix(qil, page):
+    # one 512-token chunk over a 4,096-token prefix at Qwen3-8B's head shape:
+    # 64 query tiles x KV heads, split automatically
+    w = make_custom([4608], [512], hq=32, hkv=8, page=page, seed=61 + page)
+    assert auto_splits(w, np.arange(1))
+    case = H.DeviceCase(w, DEV)
+    print(f"auto split long prefix page={page}", flush=True)
+    got = H.to_f64(case.prefill())
+    ref = H.OracleCase(w, case.data, [0]).attention([0])
+    print("  max abs err", np.max(np.abs(got - ref)), flush=True)
+    assert H.excess(got, ref, "bf16") <= 0
+
+
+@pytest.mark.parametrize("kps", [1024, 2048])
+def test_split_mixed_8b_prefill(qil, kps):
+    # the prefill part of the 8B-shaped mixed step (4 x 512 new tokens over
+    # prefixes up to 4,096): 256 query tiles x KV heads, which the automatic
+    # plan runs whole; split here on request
+    w = make_workload(5)
+    reqs = np.asarray(w.prefill_idx)
+    assert not auto_splits(w, reqs)
+    case = H.DeviceCase(w, DEV)
+    print(f"split mixed-8b prefill keys_per_split={kps}", w.cached_lens[reqs].tolist(), flush=True)
+    got = H.to_f64(case.prefill(keys_per_split=kps))
+    ref = H.OracleCase(w, case.data, reqs).attention(reqs)
+    print("  max abs err", np.max(np.abs(got - ref)), flush=True)
+    assert H.excess(got, ref, "bf16") <= 0
+
+
+def prefill_probe(page, hq=16, hkv=8):
+    """One-hot softmax in every row: each request's key at a target position
+    inside its cached prefix equals q in every dim, every other key opposes
+    it, so every weight but the target's underflows to exactly 0 and each
+    output row is that V row, whose entries are small exact integers."""
+    ctx = [40, 700, 1300, 2100, 513]
+    new = [7, 300, 129, 40, 1]
+    w = make_custom(ctx, new, hq=hq, hkv=hkv, page=page, seed=page + 7)
+    data = w.gather()
+    targets = [(97 * r + 5) % (L - n) for r, (L, n) in enumerate(zip(ctx, new))]
+    ks, vs = [], []
+    for r, L in enumerate(ctx):
+        k = np.full((L, hkv, 128), -16.0, np.float32)
+        k[targets[r]] = 16.0
+        j = np.arange(L)[:, None, None]
+        g = np.arange(hkv)[None, :, None]
+        d = np.arange(128)[None, None, :]
+        ks.append(bf16_from_f32(k))
+        vs.append(bf16_from_f32(((j * 3 + g * 5 + d + r) % 200).astype(np.float32) - 100.0))
+    data.update(k_cached=np.concatenate([k[:L - n] for k, L, n in zip(ks, ctx, new)]),
+                v_cached=np.concatenate([v[:L - n] for v, L, n in zip(vs, ctx, new)]),
+                k_new=np.concatenate([k[L - n:] for k, L, n in zip(ks, ctx, new)]),
+                v_new=np.concatenate([v[L - n:] for v, L, n in zip(vs, ctx, new)]),
+                q=bf16_from_f32(np.full((sum(new), hq, 128), 16.0, np.float32)))
+    expect = np.concatenate([np.repeat(np.repeat(vs[r][targets[r]][None], hq // hkv, axis=1), n, axis=0)
+                             for r, n in enumerate(new)])
+    return w, data, expect
+
+
+@pytest.mark.parametrize("page", [16, 64])
+def test_indexing_probe_bit_exact(qil, page):
+    w, data, expect = prefill_probe(page)
+    case = H.DeviceCase(w, DEV, data=data)
+    for kps in (0, 64, 256):
+        print(f"prefill probe page={page} keys_per_split={kps}", flush=True)
+        out = H.to_bits(case.prefill(keys_per_split=kps))
+        assert np.array_equal(out, expect), f"keys_per_split {kps}"
+
+
+def test_page_permutation_and_run_twice_bitwise(qil):
+    w = make_custom([4608, 1000], [512, 300], hq=32, hkv=8, page=16, seed=71)
+    case = H.DeviceCase(w, DEV)
+    base = H.to_bits(case.prefill(keys_per_split=256))
+    again = H.to_bits(case.prefill(keys_per_split=256))
+    assert np.array_equal(base, again)
+    perm = torch.from_numpy(np.random.default_rng(2).permutation(w.num_pages).astype(np.int64)).to(DEV)
+    kp2 = torch.empty_like(case.kp); vp2 = torch.empty_like(case.vp)
+    kp2[perm] = case.kp; vp2[perm] = case.vp
+    bt = case.bt.long()
+    case.bt = torch.where(bt >= 0, perm[bt.clamp(min=0)], bt).int()
+    case.kp, case.vp = kp2, vp2
+    moved = H.to_bits(case.prefill(keys_per_split=256))
+    assert np.array_equal(base, moved)
+
+
+def test_workspace_reused_across_calls(qil):
+    # one workspace for two split calls of different shapes in a row (the
+    # second smaller): the plan is rebuilt each call, nothing carries over
+    w1 = make_custom([4608], [512], hq=32, hkv=8, page=16, seed=81)
+    w2 = make_custom([2000, 900], [200, 64], hq=32, hkv=8, page=16, seed=82)
+    need = qil.paged_prefill_workspace_size(1, 512, 512, 4608, 32, 8, 128)
+    ws = torch.full((need,), 0xAB, dtype=torch.uint8, device=DEV)
+    for w in (w1, w2):
+        case = H.DeviceCase(w, DEV)
+        reqs = np.arange(w.batch)
+        q = case.q_all
+        out = torch.empty_like(q)
+        assert qil.paged_prefill_workspace_size(w.batch, q.shape[0], int(w.new_lens.max()),
+                                                int(w.context_lens.max()), 32, 8, 128) <= need
+        qil.paged_prefill(out, q, case.kp, case.vp, case.bt, H.i32(w.cu_seqlens(reqs), DEV), case.ctx,
+                          int(w.new_lens.max()), int(w.context_lens.max()), float(w.scale),
+                          keys_per_split=128, workspace=ws)
+        ref = H.OracleCase(w, case.data, reqs).attention(reqs)
+        assert H.excess(H.to_f64(out), ref, "bf16") <= 0
