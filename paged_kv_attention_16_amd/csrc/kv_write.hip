@@ -37,15 +37,21 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a, int rows) 
   const int eb = C / 8;  // element bytes: 16 chunks of 8 bf16, 32 chunks of 4 fp32
   const int t = r / a.num_kv_heads;
   const int g = r - t * a.num_kv_heads;
-  const int32_t slot = a.slots[t];
-  const int64_t page = slot >> a.log2_page;
-  if (slot < 0 || page >= a.num_pages) return;  // -1 = skip; out-of-range never touched
-  const int64_t off = slot & ((1 << a.log2_page) - 1);
-  const int64_t dst = ((((page * a.num_kv_heads + g) << a.log2_page) + off) * kHeadDim) * eb + c * 16;
+  // The row loads do not depend on the slot: they are issued with the slot
+  // load, so the two memory latencies overlap (a skipped token's row is read
+  // and dropped).
+  int32_t slot = a.slots[t];
   const uint4 kv = load_stream16(static_cast<const char*>(a.k) +
                                  ((int64_t)t * a.k_stride + (int64_t)g * kHeadDim) * eb + c * 16);
   const uint4 vv = load_stream16(static_cast<const char*>(a.v) +
                                  ((int64_t)t * a.v_stride + (int64_t)g * kHeadDim) * eb + c * 16);
+  // keep the row loads ahead of the branch (the compiler would sink them into it)
+  asm volatile("" : "+v"(slot) : "v"(kv.x), "v"(kv.y), "v"(kv.z), "v"(kv.w), "v"(vv.x), "v"(vv.y),
+               "v"(vv.z), "v"(vv.w));
+  const int64_t page = slot >> a.log2_page;
+  if (slot < 0 || page >= a.num_pages) return;  // -1 = skip; out-of-range never touched
+  const int64_t off = slot & ((1 << a.log2_page) - 1);
+  const int64_t dst = ((((page * a.num_kv_heads + g) << a.log2_page) + off) * kHeadDim) * eb + c * 16;
   *reinterpret_cast<uint4*>(static_cast<char*>(a.k_cache) + dst) = kv;
   *reinterpret_cast<uint4*>(static_cast<char*>(a.v_cache) + dst) = vv;
 }
