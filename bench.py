@@ -61,6 +61,10 @@ def parse():
     ap.add_argument("--skip-qkv-proj", action="store_true",
                     help="skip the QKV-projection leg (projection GEMM with the fused write as "
                          "its epilogue, vs a library GEMM followed by the fused write)")
+    ap.add_argument("--ingest-counters", metavar="DIR",
+                    help="read rocprofv3 --pmc CSVs under DIR/{fetch,write,cfetch,cwrite} "
+                         "(FETCH_SIZE / WRITE_SIZE of a bench run and of --calibrate), write "
+                         "profiles/traffic.json and print its table, then exit (no GPU)")
     ap.add_argument("--calibrate", action="store_true",
                     help="time torch's copy and sum over 1 GiB (reference ceilings and the "
                          "plain copy kernel used to scale HBM byte counters), then exit")
@@ -860,6 +864,78 @@ def sources_sha256(files):
     return h.hexdigest()
 
 
+# kernel each traffic figure is for: name prefix in the counter CSVs
+TRAFFIC_KERNELS = {
+    "decode-b256": "decode_mfma_kernel<2>",
+    "prefill-varlen": "prefill_kernel<2>",
+    "qkv-proj-8b": "qkv_proj_kernel<4, false>",
+}
+
+
+def _counter_rows(folder, counter):
+    """(kernel name, grid size, value) per dispatch from rocprofv3 --pmc CSVs."""
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(folder, "**", "*counter_collection.csv"),
+                                 recursive=True)):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                rows.append((int(r.get("Dispatch_Id", 0)), r["Kernel_Name"], int(r["Grid_Size"]),
+                             float(r["Counter_Value"])))
+    rows.sort()
+    return [(n, g, v) for _, n, g, v in rows]
+
+
+def _kernel_kib(rows, name):
+    """Mean counter value (KiB) of the last 3 dispatches of `name`'s largest grid."""
+    def short(n):
+        return n.replace("qil::(anonymous namespace)::", "").replace("void ", "").replace(" ", "")
+    mine = [(g, v) for n, g, v in rows if short(n).startswith(name.replace(" ", ""))]
+    if not mine:
+        return None
+    big = max(g for g, _ in mine)
+    vals = [v for g, v in mine if g == big][-3:]
+    return sum(vals) / len(vals)
+
+
+def ingest_counters(root):
+    """HBM bytes per launch of each leg's kernel from FETCH_SIZE / WRITE_SIZE,
+    scaled by what the same counters read for a 1 GiB device copy."""
+    fetch = _counter_rows(os.path.join(root, "fetch"), "FETCH_SIZE")
+    write = _counter_rows(os.path.join(root, "write"), "WRITE_SIZE")
+    cfetch = _counter_rows(os.path.join(root, "cfetch"), "FETCH_SIZE")
+    cwrite = _counter_rows(os.path.join(root, "cwrite"), "WRITE_SIZE")
+    copy_f = _kernel_kib(cfetch, "__amd_rocclr_copyBuffer")
+    copy_w = _kernel_kib(cwrite, "__amd_rocclr_copyBuffer")
+    if not copy_f or not copy_w:
+        sys.exit("no calibration copy in the counter CSVs")
+    gib_kib = float(1 << 20)
+    fs, ws = gib_kib / copy_f, gib_kib / copy_w
+    table = {"calibration": {"kernel": "torch copy_ of 1 GiB (__amd_rocclr_copyBuffer): reads 1 GiB, "
+                                       "writes 1 GiB",
+                             "FETCH_SIZE_KiB": round(copy_f, 1), "WRITE_SIZE_KiB": round(copy_w, 1),
+                             "fetch_scale": round(fs, 4), "write_scale": round(ws, 4)}}
+    print("| kernel | HBM read MB/launch | HBM write MB/launch |")
+    print("|---|---|---|")
+    for key, kname in TRAFFIC_KERNELS.items():
+        f, w = _kernel_kib(fetch, kname), _kernel_kib(write, kname)
+        if f is None or w is None:
+            print(f"| {kname} ({key}) | missing | missing |")
+            continue
+        fb, wb = int(f * 1024 * fs), int(w * 1024 * ws)
+        table[key] = {"kernel": kname, "source_sha256": sources_sha256(KERNEL_SOURCES[key]),
+                      "sources": list(KERNEL_SOURCES[key]), "fetch_bytes_per_launch": fb,
+                      "write_bytes_per_launch": wb, "hbm_bytes_per_launch": fb + wb}
+        print(f"| {kname} ({key}) | {fb / 1e6:.1f} | {wb / 1e6:.2f} |")
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(table, f, indent=1)
+        f.write("\n")
+    print(f"calibration: FETCH_SIZE x 1024 x {fs:.4f} + WRITE_SIZE x 1024 x {ws:.4f}")
+
+
 def traffic_for(launches_bytes_key):
     """HBM bytes per launch from committed counter runs, only while the
     kernel's sources are unchanged since the counters were taken."""
@@ -882,6 +958,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no "
               f"multi-GPU path.", file=sys.stderr)
         sys.exit(2)
+    if args.ingest_counters:
+        ingest_counters(args.ingest_counters)
+        return
     if args.calibrate:
         calibrate(args.steps)
         return

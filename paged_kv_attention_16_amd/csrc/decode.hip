@@ -312,32 +312,57 @@ constexpr int kOrderThreads = 1024;
 __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(const int32_t* context_lens,
                                                                      int batch, int max_len,
                                                                      int32_t* order) {
+  static_assert(kOrderBuckets == 4 * 64, "four wavefronts scan the buckets");
+  constexpr int kHeld = 4;  // requests per thread whose bucket stays in a register
   __shared__ int hist[kOrderBuckets];
-  __shared__ int scan[2][kOrderBuckets];
+  __shared__ int wave_sum[kOrderBuckets / 64];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   auto bucket = [&](int r) {
     int L = context_lens[r];
     L = L < 0 ? 0 : (L > max_len ? max_len : L);
     return (int)((int64_t)(max_len - L) * kOrderBuckets / ((int64_t)max_len + 1));  // 0 = longest
   };
   if (tid < kOrderBuckets) hist[tid] = 0;
-  __syncthreads();
-  for (int r = tid; r < batch; r += kOrderThreads) atomicAdd(&hist[bucket(r)], 1);
-  __syncthreads();
-  // inclusive prefix sum of the bucket counts (Hillis-Steele, 8 steps)
-  if (tid < kOrderBuckets) scan[0][tid] = hist[tid];
-  __syncthreads();
-  int src = 0;
-  for (int off = 1; off < kOrderBuckets; off <<= 1) {
-    if (tid < kOrderBuckets)
-      scan[src ^ 1][tid] = scan[src][tid] + (tid >= off ? scan[src][tid - off] : 0);
-    __syncthreads();
-    src ^= 1;
+  // the first kHeld requests of each thread: one round of loads, kept
+  int held[kHeld];
+#pragma unroll
+  for (int k = 0; k < kHeld; ++k) {
+    const int r = tid + k * kOrderThreads;
+    held[k] = r < batch ? bucket(r) : 0;
   }
-  // first free position of each bucket
-  if (tid < kOrderBuckets) hist[tid] = scan[src][tid] - hist[tid];
   __syncthreads();
-  for (int r = tid; r < batch; r += kOrderThreads) order[atomicAdd(&hist[bucket(r)], 1)] = r;
+#pragma unroll
+  for (int k = 0; k < kHeld; ++k)
+    if (tid + k * kOrderThreads < batch) atomicAdd(&hist[held[k]], 1);
+  for (int r = tid + kHeld * kOrderThreads; r < batch; r += kOrderThreads)
+    atomicAdd(&hist[bucket(r)], 1);
+  __syncthreads();
+  // first free position of each bucket: exclusive scan, a wavefront per 64 buckets
+  int own = 0, v = 0;
+  if (tid < kOrderBuckets) {
+    own = v = hist[tid];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(v, o);
+      if (lane >= o) v += t;
+    }
+    if (lane == 63) wave_sum[wv] = v;
+  }
+  __syncthreads();
+  if (tid < kOrderBuckets) {
+    int before = 0;
+    for (int i = 0; i < wv; ++i) before += wave_sum[i];
+    hist[tid] = before + v - own;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kHeld; ++k) {
+    const int r = tid + k * kOrderThreads;
+    if (r < batch) order[atomicAdd(&hist[held[k]], 1)] = r;
+  }
+  for (int r = tid + kHeld * kOrderThreads; r < batch; r += kOrderThreads)
+    order[atomicAdd(&hist[bucket(r)], 1)] = r;
 }
 
 template <int G, bool BF16>
