@@ -251,6 +251,39 @@ int qil_paged_decode(void* out, const void* q, const void* k_cache, const void* 
                      void* stream);
 
 /*
+ * qil_paged_decode_append -- the decode step's write and decode in one call:
+ * the same result as qil_kv_write(k_new, v_new, slot_mapping) followed by
+ * qil_paged_decode(...), for a batch whose new token of request r sits at
+ * position context_lens[r] - 1 ("nano-vLLM learning note", prepare_decode:
+ * the new token's slot is the block-table slot of the last position, and
+ * Attention.forward stores k/v before attending).
+ *
+ *   k_new, v_new   [batch] rows of num_kv_heads*head_dim, dtype, token strides
+ *                  in elements (>= num_kv_heads*head_dim, multiples of 8)
+ *   slot_mapping   int32 [batch]: slot_mapping[r] must be the slot of position
+ *                  context_lens[r] - 1 (block_tables[r][(L-1)/page_size] *
+ *                  page_size + (L-1) % page_size), or -1 for a padding row
+ *                  (nothing is stored; that row's output is unspecified);
+ *                  QIL_DEBUG checks it
+ *   other arguments as qil_paged_decode (workspace sized by
+ *   qil_paged_decode_workspace_size).
+ * bf16 runs one kernel (plus the ordering and merge passes of the split
+ * plan): the split that holds each request's last key reads that key's rows
+ * from k_new / v_new instead of the pool and stores them at their slot, so
+ * the pool row is written and used in the same launch.  fp32 runs the write
+ * and the decode as two kernels.  batch == 0 is a no-op.
+ */
+int qil_paged_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
+                            int64_t k_token_stride, int64_t v_token_stride,
+                            const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                            const int32_t* block_tables, int32_t block_table_stride,
+                            const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                            int32_t num_pages, int32_t max_context_len, float scale, int32_t dtype,
+                            int32_t keys_per_split, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
  * qil_paged_prefill -- chunked varlen causal prefill over the paged cache
  * ("nano-vLLM learning note", Attention.forward prefill branch with cached
  * prefix and prepare_prefill: positions start at num_cached_tokens;

@@ -10,6 +10,7 @@ The functions mirror the C ABI in include/qil.h:
   kv_write(k, v, k_cache, v_cache, slot_mapping, page_size=..., fuse=None)
   rope_cos_sin(table, theta)
   paged_decode(out, q, k_cache, v_cache, block_tables, context_lens, ...)
+  paged_decode_append(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, ...)
   paged_prefill(out, q, k_cache, v_cache, block_tables, cu_seqlens_q, context_lens, ...)
   paged_attention_mixed(k_cache, v_cache, scale, decode=..., prefill=...)
   qkv_proj_write(x, weight, k_cache, v_cache, slot_mapping, q_out, ...)
@@ -21,7 +22,8 @@ import os
 
 __all__ = [
     "QilError", "lib_path", "load", "version", "kv_write", "QKNormRope", "rope_cos_sin",
-    "paged_decode", "paged_decode_workspace_size", "paged_prefill", "paged_prefill_workspace_size",
+    "paged_decode", "paged_decode_workspace_size", "paged_decode_append", "paged_prefill",
+    "paged_prefill_workspace_size",
     "paged_attention_mixed",
     "qkv_proj_write", "qkv_proj_workspace_size", "set_debug", "debug_enabled",
     "QIL_F32", "QIL_BF16",
@@ -108,6 +110,10 @@ def load(path=None):
     lib.qil_paged_decode.restype = ctypes.c_int
     lib.qil_paged_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
                                      i32, f32, i32, i32, vp, sz, vp]
+    lib.qil_paged_decode_append.restype = ctypes.c_int
+    lib.qil_paged_decode_append.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int64, vp, vp,
+                                            vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32,
+                                            f32, i32, i32, vp, sz, vp]
     lib.qil_paged_attention_mixed.restype = ctypes.c_int
     lib.qil_paged_attention_mixed.argtypes = [ctypes.POINTER(_DecodeBatchC),
                                               ctypes.POINTER(_PrefillBatchC), vp, vp, i32, i32,
@@ -270,6 +276,28 @@ def paged_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_conte
         int(block_tables.shape[1]), _ptr(context_lens), batch, hq, hkv, d, page, num_pages,
         int(max_context_len), float(scale), _dtype_code(q), int(keys_per_split),
         _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc)
+
+
+def paged_decode_append(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
+                        context_lens, max_context_len, scale, keys_per_split=0, workspace=None,
+                        stream=None):
+    """The decode step's write and decode in one call: k_new, v_new [B, Hkv, 128]
+    (token stride = stride(0)), slot_mapping int32 [B] = slot of each request's
+    last position; otherwise as paged_decode."""
+    import torch
+    num_pages, hkv, page, d = _pool_shape(k_cache)
+    batch, hq = int(q.shape[0]), int(q.shape[1])
+    need = paged_decode_workspace_size(batch, hq, hkv, int(max_context_len), page, keys_per_split)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load().qil_paged_decode_append(
+        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), int(k_new.stride(0)), int(v_new.stride(0)),
+        _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(context_lens), batch, hq, hkv, d, page, num_pages,
+        int(max_context_len), float(scale), _dtype_code(q), int(keys_per_split), _ptr(workspace),
+        ws_bytes, _stream(stream))
     _check(rc)
 
 

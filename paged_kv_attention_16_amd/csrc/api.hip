@@ -78,6 +78,11 @@ int describe(const qil::DebugReport& r) {
     case qil::kChunkTooLong:
       return fail(QIL_EINVAL, "QIL_DEBUG: request %d has %d new tokens but context_len %d", r.i,
                   r.j, r.value);
+    case qil::kAppendSlot:
+      return fail(QIL_EINVAL,
+                  "QIL_DEBUG: slot_mapping[%d] = %d is not the slot %d of the request's last "
+                  "position",
+                  r.i, r.value, r.j);
     case qil::kChunkAboveMax:
       return fail(QIL_EINVAL, "QIL_DEBUG: request %d has %d new tokens, above max_seqlen_q %d",
                   r.i, r.j, r.value);
@@ -652,6 +657,66 @@ int qil_paged_decode(void* out, const void* q, const void* k_cache, const void* 
     if (rc) return rc;
   }
   hipError_t e = qil::launch_decode(a, s);
+  if (e != hipSuccess) return fail(QIL_EHIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int qil_paged_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
+                            int64_t k_token_stride, int64_t v_token_stride,
+                            const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                            const int32_t* block_tables, int32_t block_table_stride,
+                            const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                            int32_t num_pages, int32_t max_context_len, float scale, int32_t dtype,
+                            int32_t keys_per_split, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  qil::DecodeArgs a;
+  bool empty = false;
+  int rc = prep_decode(out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens,
+                       batch, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                       max_context_len, scale, dtype, keys_per_split, workspace, workspace_bytes,
+                       a, &empty);
+  if (rc || empty) return rc;
+  if (!k_new || !v_new || !slot_mapping) return fail(QIL_EINVAL, "null pointer argument");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(QIL_EINVAL, "k_new and v_new must be 16-byte aligned");
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (k_token_stride < row || v_token_stride < row || k_token_stride % 8 || v_token_stride % 8)
+    return fail(QIL_EINVAL, "token strides (%lld, %lld) must be >= num_kv_heads*head_dim %lld and "
+                "multiples of 8", (long long)k_token_stride, (long long)v_token_stride,
+                (long long)row);
+  if ((int64_t)num_pages * page_size > INT32_MAX)
+    return fail(QIL_EINVAL, "num_pages*page_size exceeds the int32 slot range");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_on()) {
+    const int64_t num_slots = (int64_t)num_pages * page_size;
+    rc = run_checks(s, [&](qil::DebugReport* rep) {
+      hipError_t e = check_decode_metadata(a, rep, s);
+      if (e == hipSuccess) e = qil::launch_check_slots(slot_mapping, batch, num_slots, rep, s);
+      if (e == hipSuccess)
+        e = qil::launch_check_append(slot_mapping, block_tables, block_table_stride, context_lens,
+                                     batch, a.log2_page, rep, s);
+      return e;
+    });
+    if (rc) return rc;
+  }
+  hipError_t e;
+  if (a.bf16) {
+    // one kernel: the split holding each request's last key takes the new
+    // rows from k_new / v_new and stores them
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_new_stride = k_token_stride;
+    a.v_new_stride = v_token_stride;
+    a.new_slots = slot_mapping;
+    e = qil::launch_decode(a, s);
+  } else {
+    // fp32: the plain write, then the decode
+    qil::KvWriteArgs w{k_new, v_new, k_token_stride, v_token_stride, k_cache, v_cache,
+                       slot_mapping, batch, num_kv_heads, a.log2_page, num_pages, 4};
+    e = qil::launch_kv_write(w, s);
+    if (e == hipSuccess) e = qil::launch_decode(a, s);
+  }
   if (e != hipSuccess) return fail(QIL_EHIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
 }

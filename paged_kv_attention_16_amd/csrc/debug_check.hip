@@ -76,6 +76,20 @@ __global__ void tables_kernel(const int32_t* bt, int32_t stride, const int32_t* 
   }
 }
 
+// Decode with append: request r's new token goes to the slot of its last
+// position, or nowhere (-1); its context already passed tables_kernel.
+__global__ void append_kernel(const int32_t* slots, const int32_t* bt, int32_t stride,
+                              const int32_t* ctx, int32_t batch, int32_t log2_page,
+                              DebugReport* rep) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= batch) return;
+  const int32_t pos = ctx[r] - 1;
+  if (pos < 0 || slots[r] == -1) return;  // -1: no pool write for this request
+  const int32_t want = (bt[(int64_t)r * stride + (pos >> log2_page)] << log2_page) +
+                       (pos & ((1 << log2_page) - 1));
+  if (slots[r] != want) report(rep, kAppendSlot, r, want, slots[r]);
+}
+
 // cu_seqlens: starts at 0, non-decreasing, ends at total_q; each request's
 // new tokens fit its context and max_seqlen_q.
 __global__ void cu_kernel(const int32_t* cu, const int32_t* ctx, int32_t batch, int32_t total_q,
@@ -144,6 +158,15 @@ hipError_t launch_check_tables(const int32_t* block_tables, int32_t bt_stride,
   if (batch <= 0) return hipSuccess;
   hipLaunchKernelGGL(tables_kernel, dim3(batch), dim3(256), 0, s, block_tables, bt_stride,
                      context_lens, log2_page, num_pages, max_context_len, rep);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_append(const int32_t* slots, const int32_t* block_tables, int32_t bt_stride,
+                               const int32_t* context_lens, int32_t batch, int32_t log2_page,
+                               DebugReport* rep, hipStream_t s) {
+  if (batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(append_kernel, dim3((batch + 255) / 256), dim3(256), 0, s, slots,
+                     block_tables, bt_stride, context_lens, batch, log2_page, rep);
   return hipGetLastError();
 }
 

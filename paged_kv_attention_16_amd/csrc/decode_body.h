@@ -100,6 +100,22 @@ __device__ __forceinline__ void decode_mfma_split(const DecodeArgs& a, int split
 
   char* ring = &smem[w][0][0][0];
 
+  // Append: the new token's key L - 1 lies in this split.  The wavefront
+  // whose group holds it takes its K and V rows from the inputs (lanes 0-15
+  // one 16-byte chunk of K each, lanes 16-31 of V), writes them over that
+  // row of its LDS tile once the tile has landed, so the pool is never read
+  // for that row, and stores them at the token's slot after its last group.
+  // The row load is issued behind the first group's tile loads, so the
+  // count waits of the ring cover it without delaying the stream.
+  const int app_rel = a.k_new != nullptr && L - 1 >= kbeg && L - 1 < kend ? L - 1 - kbeg : -1;
+  const int app_w = app_rel >= 0 ? (app_rel >> 4) % W : -1;
+  const int app_i = app_rel >= 0 ? app_rel / (16 * W) : -1;
+  const int app_row = app_rel & 15;
+  const bool app_lane = w == app_w && lane < 32;
+  const int app_c = lane & 15;
+  const bool app_is_v = lane >= 16;
+  uint4 app_val = make_uint4(0u, 0u, 0u, 0u);
+
   const int32_t* bt_row = a.block_tables + (int64_t)r * a.bt_stride;
   const char* kpool = static_cast<const char*>(a.k_cache);
   const char* vpool = static_cast<const char*>(a.v_cache);
@@ -216,6 +232,11 @@ __device__ __forceinline__ void decode_mfma_split(const DecodeArgs& a, int split
 #pragma unroll
   for (int i = 0; i < kMD - 1; ++i)
     if (i < ngroups) issue(i);
+  if (app_lane) {
+    const uint16_t* src = static_cast<const uint16_t*>(app_is_v ? a.v_new : a.k_new) +
+                          (int64_t)r * (app_is_v ? a.v_new_stride : a.k_new_stride) + g * kHeadDim;
+    app_val = *reinterpret_cast<const uint4*>(src + 8 * app_c);
+  }
   for (int i = 0; i < ngroups; ++i) {
     // refill the slot computed at i - 1 (its LDS reads are complete), then
     // wait until group i has landed: the groups issued after it may still fly
@@ -225,9 +246,34 @@ __device__ __forceinline__ void decode_mfma_split(const DecodeArgs& a, int split
     else if (kMD > 2 && ahead == 2) wait_vmcnt<16>();
     else if (ahead == 1) wait_vmcnt<8>();
     else wait_vmcnt<0>();
+    if (w == app_w && i == app_i) {
+      // The tile has landed (the count wait above): overwrite the new
+      // token's row.  When it is the group's first row, the rows past the
+      // context were loaded as copies of it (stale pool contents): they get
+      // the new row too, since their weights are 0 but must multiply finite
+      // values.  This wavefront's LDS reads below come after the writes.
+      char* kt = ring + (i % kMD) * 2 * kTile;
+      const int last = app_row == 0 ? 15 : app_row;
+      for (int row = app_row; row <= last; ++row) {
+        if (lane < 16)
+          *reinterpret_cast<uint4*>(kt + row * 256 + 16 * mk_chunk(row, lane)) = app_val;
+        else if (lane < 32)
+          *reinterpret_cast<uint4*>(kt + kTile + row * 256 + 16 * mv_chunk(row, lane - 16)) = app_val;
+      }
+    }
     compute(i);
   }
   static_assert(kMD >= 2 && kMD <= 4, "the wait ladder above covers 1 to 3 groups in flight");
+  if (app_lane) {
+    const int32_t slot = a.new_slots[r];
+    const int64_t page = slot >> a.log2_page;
+    if (slot >= 0 && page < a.num_pages) {
+      const int64_t prow = ((page * a.num_kv_heads + g) << a.log2_page) + (slot & (P - 1));
+      // the append entry point hands over writable pools
+      char* pool = const_cast<char*>(static_cast<const char*>(app_is_v ? a.v_cache : a.k_cache));
+      *reinterpret_cast<uint4*>(pool + prow * 256 + 16 * app_c) = app_val;
+    }
+  }
 
   // Row sums over the four lanes of each head.
   lsum = swap_sum32(swap_sum16(lsum));

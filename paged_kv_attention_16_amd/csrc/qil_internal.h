@@ -97,6 +97,16 @@ struct DecodeArgs {
   int32_t* order;          // [batch] requests by decreasing context length, or null
                            // (then request r is grid row r)
   bool bf16;
+  // Append (bf16 matrix-core kernel only; null = plain decode): request r's
+  // new token at position context_lens[r] - 1 has K/V rows k_new/v_new
+  // [r][Hkv][128] (token strides in elements).  The split that holds that
+  // key takes the rows from these inputs instead of the pool and stores them
+  // at new_slots[r].
+  const void* k_new;
+  const void* v_new;
+  int64_t k_new_stride;
+  int64_t v_new_stride;
+  const int32_t* new_slots;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
@@ -176,6 +186,7 @@ enum DebugCode : int32_t {
   kBadCuSeqlens = 6,  // i = index into cu_seqlens, value = entry
   kChunkTooLong = 7,  // i = request, j = new tokens, value = context length
   kChunkAboveMax = 8, // i = request, j = new tokens, value = max_seqlen_q
+  kAppendSlot = 9,    // i = request, j = expected slot, value = slot_mapping entry
 };
 
 // Device address of this device's report (resolved once per device).
@@ -191,5 +202,9 @@ hipError_t launch_check_tables(const int32_t* block_tables, int32_t bt_stride,
                                hipStream_t s);
 hipError_t launch_check_cu(const int32_t* cu, const int32_t* context_lens, int32_t batch,
                            int32_t total_q, int32_t max_seqlen_q, DebugReport* rep, hipStream_t s);
+// slot_mapping[r] is the slot of position context_lens[r] - 1 (decode with append)
+hipError_t launch_check_append(const int32_t* slots, const int32_t* block_tables, int32_t bt_stride,
+                               const int32_t* context_lens, int32_t batch, int32_t log2_page,
+                               DebugReport* rep, hipStream_t s);
 
 }  // namespace qil

@@ -12,8 +12,10 @@ its decode throughput.
 
 `DecodeStepGraph` does the same for the attention part of the step.  It owns
 static buffers sized for one bucket, pads a smaller batch up to the bucket,
-captures `layers x (qil_kv_write, qil_paged_decode)` into a HIP graph
-(torch.cuda.CUDAGraph, which is hipGraph on ROCm) and replays it.  Every
+captures `layers x qil_paged_decode_append` (the write fused into the decode
+kernel; `fused_write=False` captures `qil_kv_write, qil_paged_decode`
+instead) into a HIP graph (torch.cuda.CUDAGraph, which is hipGraph on ROCm)
+and replays it.  Every
 kernel in the graph is a libqil kernel; the library calls contain no host
 synchronisation, allocation or memset, so they capture as they are.
 
@@ -57,7 +59,7 @@ class DecodeStepGraph:
     """
 
     def __init__(self, pools, bucket, num_q_heads, bt_stride, max_context_len, scale,
-                 pad_page=0, keys_per_split=0):
+                 pad_page=0, keys_per_split=0, fused_write=True):
         import torch
         self.pools = list(pools)
         k0 = self.pools[0][0]
@@ -70,6 +72,7 @@ class DecodeStepGraph:
         self.scale = float(scale)
         self.pad_page = int(pad_page)
         self.keys_per_split = int(keys_per_split)
+        self.fused_write = bool(fused_write)
         B, dev = self.bucket, self.device
         if self.max_context_len > self.bt_stride * page:
             raise qil.QilError(1, "max_context_len exceeds bt_stride * page_size")
@@ -91,6 +94,13 @@ class DecodeStepGraph:
     def run_eager(self):
         """Issue the step's launches on the current stream."""
         for l, (kc, vc) in enumerate(self.pools):
+            if self.fused_write:
+                qil.paged_decode_append(self.out[l], self.q[l], self.k_new[l], self.v_new[l],
+                                        self.slots, kc, vc, self.block_tables, self.context_lens,
+                                        self.max_context_len, self.scale,
+                                        keys_per_split=self.keys_per_split,
+                                        workspace=self.workspace)
+                continue
             qil.kv_write(self.k_new[l], self.v_new[l], kc, vc, self.slots)
             qil.paged_decode(self.out[l], self.q[l], kc, vc, self.block_tables, self.context_lens,
                              self.max_context_len, self.scale, keys_per_split=self.keys_per_split,

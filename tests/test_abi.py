@@ -195,6 +195,33 @@ def test_prefill_split_workspace(lib):
     assert ws(1, 512, 512, 8192, 32, 8, 8192) == 0       # one piece covers every tile
 
 
+def app(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, kn=FAKE, vn=FAKE, ks=1024, vs=1024, slots=FAKE, kc=FAKE, vc=FAKE,
+             bt=FAKE, bts=128, ctx=FAKE, B=4, hq=16, hkv=8, d=128, page=16, pages=100, maxL=2048,
+             scale=0.088, dtype=1, S=0, ws=None, wsb=0)
+    a.update(kw)
+    return lib.qil_paged_decode_append(a["out"], a["q"], a["kn"], a["vn"], a["ks"], a["vs"],
+                                       a["slots"], a["kc"], a["vc"], a["bt"], a["bts"], a["ctx"],
+                                       a["B"], a["hq"], a["hkv"], a["d"], a["page"], a["pages"],
+                                       a["maxL"], a["scale"], a["dtype"], a["S"], a["ws"], a["wsb"],
+                                       None)
+
+
+def test_decode_append_validation(lib):
+    need = lib.qil_paged_decode_workspace_size(4, 16, 8, 2048, 16, 0)
+    ok = dict(ws=FAKE, wsb=need)
+    assert app(lib, B=0) == 0
+    assert app(lib, kn=None, **ok) == EINVAL
+    assert app(lib, slots=None, **ok) == EINVAL
+    assert app(lib, vn=FAKE + 4, **ok) == EINVAL        # misaligned
+    assert app(lib, ks=1000, **ok) == EINVAL            # below num_kv_heads*head_dim
+    assert app(lib, vs=1028, **ok) == EINVAL            # not a multiple of 8
+    assert app(lib, hq=24, **ok) == EUNSUP
+    assert app(lib, dtype=3, **ok) == EUNSUP
+    if need > 0:
+        assert app(lib) == EWS                          # workspace missing
+
+
 def test_rope_table_validation(lib):
     assert lib.qil_rope_cos_sin(None, 10, 128, 1e6, None) == EINVAL
     assert lib.qil_rope_cos_sin(FAKE, 0, 128, 1e6, None) == EINVAL

@@ -1,5 +1,6 @@
-"""Decode step captured into a HIP graph at a padded batch bucket: every
-replay equals the eager launches bit for bit (same kernels, same split plan),
+"""Decode step captured into a HIP graph at a padded batch bucket, with the
+write fused into decode and as two calls: every replay equals the eager
+write + decode launches bit for bit (same split plan),
 with eager work and synchronisations between replays; a smaller batch padded
 into the same graph gives the same rows; and the graph's output matches the
 oracle."""
@@ -43,7 +44,8 @@ def eager_decode(case, w, max_l, keys_per_split):
     return out
 
 
-def test_graph_replays_equal_eager(qil):
+@pytest.mark.parametrize("fused_write", [True, False])
+def test_graph_replays_equal_eager(qil, fused_write):
     from paged_kv_attention_16_amd.graph import DecodeStepGraph, bucket_for
     ctx = [7, 300, 1025, 64, 513]
     cases = layer_cases(ctx, 2)
@@ -53,7 +55,7 @@ def test_graph_replays_equal_eager(qil):
     max_l, S = 2048, 256   # a fixed split size: the eager reference has the same plan
     g = DecodeStepGraph([(c.kp, c.vp) for _, c in cases], bucket, w0.num_q_heads,
                         w0.block_tables.shape[1] + 64, max_l, float(w0.scale), pad_page=0,
-                        keys_per_split=S)
+                        keys_per_split=S, fused_write=fused_write)
     g.update(cases[0][1].new_slots, cases[0][1].bt, cases[0][1].ctx,
              q=[c.q_all for _, c in cases], k_new=[c.k_new for _, c in cases],
              v_new=[c.v_new for _, c in cases])

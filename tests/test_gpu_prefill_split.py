@@ -146,3 +146,22 @@ def test_workspace_reused_across_calls(qil):
                           keys_per_split=128, workspace=ws)
         ref = H.OracleCase(w, case.data, reqs).attention(reqs)
         assert H.excess(H.to_f64(out), ref, "bf16") <= 0
+
+
+def test_split_with_zero_length_and_tiny_requests(qil):
+    # a request with no new tokens in this call and a one-token context sit
+    # between long-prefix chunks: their query tiles give no pieces
+    w = make_custom([3000, 20, 1, 2500], [300, 20, 1, 64], hq=32, hkv=8, page=16, seed=91)
+    case = H.DeviceCase(w, DEV)
+    keep = [0, 2, 3]                      # request 1 gets no new tokens in this call
+    rows = torch.from_numpy(case.rows_of(keep)).to(DEV)
+    q = case.q_all.index_select(0, rows).contiguous()
+    cu = H.i32([0, 300, 300, 301, 365], DEV)
+    ctx = H.i32([3000, 19, 1, 2500], DEV)
+    for kps in (0, 256):
+        print(f"split with an empty request, keys_per_split={kps}", flush=True)
+        out = torch.empty_like(q)
+        qil.paged_prefill(out, q, case.kp, case.vp, case.bt, cu, ctx, 300, 3000, float(w.scale),
+                          keys_per_split=kps)
+        ref = H.OracleCase(w, case.data, keep).attention(keep)
+        assert H.excess(H.to_f64(out), ref, "bf16") <= 0
