@@ -268,13 +268,15 @@ def gpu_legs(args):
     step_bytes = kv_bytes + w.decode_io_bytes() + write_bytes(w, w.batch)
     dec_bytes = kv_bytes + w.decode_io_bytes()
     wall0 = time.perf_counter()
-    # the step as two calls (qil_kv_write, then qil_paged_decode) ...
-    t = timed_steps([write, decode], args.steps, args.warmup, flush, stream)
-    # ... and as one qil_paged_decode_append call (the headline step)
+    # the step as one qil_paged_decode_append call (the headline step) ...
     tf = timed_steps([append], args.steps, args.warmup, flush, stream)
-    wall = time.perf_counter() - wall0
-    # the one-call step with warm caches (no flush): a labelled secondary number
+    # ... the same with warm caches (no flush): a labelled secondary number ...
     th = timed_steps([append], args.steps, args.warmup, None, stream)
+    # ... and as two calls (qil_kv_write, then qil_paged_decode): the decode
+    # call alone is the roofline kernel (run last, so counter runs that keep
+    # the last launches of the largest decode grid see this call)
+    t = timed_steps([write, decode], args.steps, args.warmup, flush, stream)
+    wall = time.perf_counter() - wall0
     res["decode"] = dict(
         workload=w, step_ms=tf["step_mean"], step_ms_median=tf["step_median"],
         step_ms_p10=tf["step_p10"], step_ms_p90=tf["step_p90"],
@@ -994,9 +996,7 @@ def main():
     dec = res["decode"]
     w = dec["workload"]
     value = dec["step_bytes"] / (dec["step_ms"] * 1e-3) / 1e9
-    # the headline call is the whole step: its bytes are the step's
-    achieved = value
-    two_call_dec = dec["dec_bytes"] / (dec["dec_ms"] * 1e-3) / 1e9
+    achieved = dec["dec_bytes"] / (dec["dec_ms"] * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -1024,30 +1024,35 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "qil_paged_decode_append: decode_order_kernel (longest requests first) then "
-                      "decode_mfma_kernel<2> with the new tokens' K/V write fused in, one split "
-                      "per request, no merge pass; the launch time covers both",
+            "kernel": "qil_paged_decode (the decode call of the two-call step): decode_order_kernel "
+                      "(longest requests first) then decode_mfma_kernel<2>, one split per request, "
+                      "no merge pass; the launch time covers both",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_for("decode-b256"),
-            "algorithmic_bytes_per_launch": int(dec["step_bytes"]),
-            "launch_us_mean": round(dec["step_ms"] * 1e3, 2),
-            "launch_timing": "mean time of the call, events only around it",
-            "event_bracket_us_mean": round(dec["step_bracket_ms"] * 1e3, 2),
-            "event_bracket_us_median": round(dec["step_bracket_ms_median"] * 1e3, 2),
+            "algorithmic_bytes_per_launch": int(dec["dec_bytes"]),
+            "launch_us_mean": round(dec["dec_ms"] * 1e3, 2),
+            "launch_timing": "mean two-call step time with no marker between the kernels, minus the "
+                             "separately bracketed write",
+            "event_bracket_us_mean": round(dec["dec_bracket_ms"] * 1e3, 2),
             "measured_ceiling": res["ceilings"]["stream_read_GB_s"],
             "frac_of_measured": round(achieved / res["ceilings"]["stream_read_GB_s"], 4),
+        },
+        "fused_step": {
+            "call": "qil_paged_decode_append: the 256 new tokens' K/V write fused into the decode "
+                    "kernel (value and ms_per_step)",
+            "GB_per_s": round(value, 1),
+            "frac": round(value / HBM_PEAK_GBS, 4),
+            "event_bracket_us_mean": round(dec["step_bracket_ms"] * 1e3, 2),
+            "event_bracket_us_median": round(dec["step_bracket_ms_median"] * 1e3, 2),
             "hot_no_flush_GB_s": round(dec["step_bytes"] / (dec["hot_step_ms"] * 1e-3) / 1e9, 1),
         },
         "two_call_step": {
             "calls": "qil_kv_write (256 tokens) then qil_paged_decode",
             "step_us": round(dec["two_call_step_ms"] * 1e3, 2),
             "GB_per_s": round(dec["step_bytes"] / (dec["two_call_step_ms"] * 1e-3) / 1e9, 1),
-            "decode_launch_us": round(dec["dec_ms"] * 1e3, 2),
-            "decode_GB_per_s": round(two_call_dec, 1),
-            "decode_frac": round(two_call_dec / HBM_PEAK_GBS, 4),
             "write_bracket_us": round(dec["write_ms"] * 1e3, 2),
         },
         "step_us": {"mean": round(dec["step_ms"] * 1e3, 2), "median": round(dec["step_ms_median"] * 1e3, 2),
