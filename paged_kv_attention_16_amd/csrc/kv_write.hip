@@ -74,12 +74,6 @@ __global__ __launch_bounds__(256) void kv_write_fused_kernel(KvWriteArgs a, Fuse
   const int head = is_q ? kind_row : (is_k ? kind_row - f.num_q_heads
                                            : kind_row - f.num_q_heads - a.num_kv_heads);
 
-  const int32_t slot = a.slots[t];
-  const int64_t page = slot >> a.log2_page;
-  const bool store_kv = slot >= 0 && page < a.num_pages;
-  const int64_t dst_row =
-      ((page * a.num_kv_heads + head) << a.log2_page) + (slot & ((1 << a.log2_page) - 1));
-
   const uint16_t* src;
   if (is_q)
     src = static_cast<const uint16_t*>(f.q) + (int64_t)t * f.q_stride + head * kHeadDim;
@@ -87,7 +81,22 @@ __global__ __launch_bounds__(256) void kv_write_fused_kernel(KvWriteArgs a, Fuse
     src = static_cast<const uint16_t*>(a.k) + (int64_t)t * a.k_stride + head * kHeadDim;
   else
     src = static_cast<const uint16_t*>(a.v) + (int64_t)t * a.v_stride + head * kHeadDim;
+  // The row, its slot, its position and its norm weights do not depend on
+  // one another: the four loads are issued together (v rows load weights
+  // and a position they do not use), and an empty asm barrier that takes
+  // them keeps the compiler from sinking any of them behind another's wait.
+  // Only the cos/sin load waits for the position.
+  int32_t slot = a.slots[t];
+  int pos = f.positions[t];
   const uint4 raw = load_stream16(reinterpret_cast<const char*>(src + 8 * j));
+  const uint4 wraw = *reinterpret_cast<const uint4*>(
+      static_cast<const uint16_t*>(is_q ? f.q_w : f.k_w) + 8 * j);
+  asm volatile("" : "+v"(slot), "+v"(pos) : "v"(raw.x), "v"(raw.y), "v"(raw.z), "v"(raw.w),
+               "v"(wraw.x), "v"(wraw.y), "v"(wraw.z), "v"(wraw.w));
+  const int64_t page = slot >> a.log2_page;
+  const bool store_kv = slot >= 0 && page < a.num_pages;
+  const int64_t dst_row =
+      ((page * a.num_kv_heads + head) << a.log2_page) + (slot & ((1 << a.log2_page) - 1));
 
   if (!is_q && !is_k) {  // v: raw copy
     if (store_kv)
@@ -108,8 +117,6 @@ __global__ __launch_bounds__(256) void kv_write_fused_kernel(KvWriteArgs a, Fuse
   ss = row_sum16(ss);  // the 16 lanes of the row
   const float inv_rms = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + f.eps);
 
-  const uint4 wraw = *reinterpret_cast<const uint4*>(
-      static_cast<const uint16_t*>(is_q ? f.q_w : f.k_w) + 8 * j);
   const uint32_t ww[4] = {wraw.x, wraw.y, wraw.z, wraw.w};
   float y[8];
 #pragma unroll
@@ -122,7 +129,6 @@ __global__ __launch_bounds__(256) void kv_write_fused_kernel(KvWriteArgs a, Fuse
     y[2 * i + 1] = bf16_hi(m);
   }
 
-  int pos = f.positions[t];
   pos = pos < 0 ? 0 : (pos >= f.max_position ? f.max_position - 1 : pos);
   const float* cs = f.cos_sin + (int64_t)pos * kHeadDim + 8 * (j & 7);
   const float4 c0 = *reinterpret_cast<const float4*>(cs);
