@@ -304,7 +304,7 @@ int qil_paged_decode_append(void* out, const void* q, const void* k_new, const v
  *                  pieces of near-equal length (at most 32 pieces: a smaller
  *                  value is raised to fit), each run by its own workgroup, and
  *                  the pieces are merged by the log-sum-exp rule.  Automatic
- *                  splitting applies when the call has fewer than 160 query
+ *                  splitting applies when the call has at most 128 query
  *                  tiles x KV heads and max_context_len is at least 2,048, e.g.
  *                  a chunk of a long prompt.  Splitting needs
  *                  batch * ceil(max_seqlen_q / (256/G)) <= 4096; larger calls

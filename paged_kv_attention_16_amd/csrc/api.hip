@@ -316,14 +316,14 @@ int prep_decode(void* out, const void* q, const void* k_cache, const void* v_cac
 
 // Split plan of a prefill call (host integers only).  The grid of whole
 // query tiles has one workgroup per CU at a time (8 waves of 205 registers);
-// when it holds fewer than 160 tiles with rows, one round of long tiles sets
-// the time while most CUs idle.  Such calls cut every query tile into pieces
-// of at most S 64-key tiles, S chosen for one piece per CU if every tile were
-// as long as the longest possible one, and at least 16 key tiles.  Each
-// piece loads its queries and writes a partial row block, and the split adds
-// a planning and a merge launch, so shorter pieces or busier grids cost more
-// than they balance (measured on one chunk over a long prefix, and on the
-// 8B mixed step's 256 tiles, where whole tiles stay faster).
+// when it holds at most 128 tiles with rows, one round of long tiles sets
+// the time while half the CUs or more idle.  Such calls cut every query tile
+// into n = 256 / tiles pieces (rounded down: all pieces still fit one round),
+// that is at most S = ceil(kt_max / n) 64-key tiles each, and at least 16.
+// Each piece loads its queries and writes a partial row block, and the split
+// adds a planning and a merge launch, so shorter pieces or busier grids cost
+// more than they balance (measured on one chunk over a long prefix, and on
+// the 8B mixed step's 256 tiles, where whole tiles stay faster).
 struct PrefillPlan {
   int32_t S = 0;            // 0: unsplit
   int32_t pieces = 1;       // pieces of the longest possible tile
@@ -333,7 +333,7 @@ struct PrefillPlan {
 };
 
 constexpr int32_t kMaxPrefillKeysPerSplit = 64 * 1023;
-constexpr int32_t kAutoSplitTiles = 160;   // auto-split below this many query tiles x KV heads
+constexpr int32_t kAutoSplitTiles = 128;   // auto-split up to this many query tiles x KV heads
 constexpr int32_t kMinPieceTiles = 16;
 
 PrefillPlan plan_prefill(int32_t batch, int32_t total_q, int32_t max_seqlen_q,
@@ -355,8 +355,9 @@ PrefillPlan plan_prefill(int32_t batch, int32_t total_q, int32_t max_seqlen_q,
     S = keys_per_split / 64;
   } else {
     const int64_t tiles = entries * num_kv_heads;
-    if (tiles >= kAutoSplitTiles || kt_max < 2 * kMinPieceTiles) return p;
-    S = std::max<int64_t>(kMinPieceTiles, (kt_max * tiles + 255) / 256);
+    if (tiles > kAutoSplitTiles || kt_max < 2 * kMinPieceTiles) return p;
+    const int64_t n = 256 / tiles;  // >= 2
+    S = std::max<int64_t>(kMinPieceTiles, (kt_max + n - 1) / n);
   }
   S = std::min<int64_t>(S, qil::kMaxPieceTiles);
   if ((kt_max + S - 1) / S > qil::kMaxPieces) S = (kt_max + qil::kMaxPieces - 1) / qil::kMaxPieces;
