@@ -283,8 +283,9 @@ def paged_decode_append(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, bl
                         context_lens, max_context_len, scale, keys_per_split=0, workspace=None,
                         stream=None):
     """The decode step's write and decode in one call: k_new, v_new [B, Hkv, 128]
-    (token stride = stride(0)), slot_mapping int32 [B] = slot of each request's
-    last position; otherwise as paged_decode."""
+    (or row views with a token stride, as kv_write), slot_mapping int32 [B] =
+    slot of each request's last position (-1: padding row); otherwise as
+    paged_decode."""
     import torch
     num_pages, hkv, page, d = _pool_shape(k_cache)
     batch, hq = int(q.shape[0]), int(q.shape[1])
@@ -293,7 +294,8 @@ def paged_decode_append(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, bl
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = load().qil_paged_decode_append(
-        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), int(k_new.stride(0)), int(v_new.stride(0)),
+        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _token_stride(k_new, hkv * d),
+        _token_stride(v_new, hkv * d),
         _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         int(block_tables.shape[1]), _ptr(context_lens), batch, hq, hkv, d, page, num_pages,
         int(max_context_len), float(scale), _dtype_code(q), int(keys_per_split), _ptr(workspace),
