@@ -8,20 +8,20 @@
 // and its RotaryEmbedding block for the cos/sin table.
 //
 // The plain write is a bandwidth-bound copy: a thread moves one 16-byte chunk
-// of one (token, head) row, so a wavefront moves 4 (bf16) or 2 (fp32) whole
-// 128-element rows per instruction with coalesced 16-byte accesses.
+// of each of two (token, head) rows, so a wavefront moves 4 (bf16) or 2 (fp32)
+// whole 128-element rows per instruction with coalesced 16-byte accesses.
 #include "device_common.h"
 #include "qil_internal.h"
 
 namespace qil {
 namespace {
 
-// One thread moves one 16-byte chunk of one (token, kv head) row of K and of
-// V: C = row bytes / 16 consecutive threads cover a row.  The new rows are
-// read exactly once, so their loads are non-temporal (measured faster than
-// plain loads, and faster than several rows per thread); the stores stay
-// cached, since attention reads the rows back right after.  Indices are
-// 32-bit (rows = tokens x heads <= 2^30); pool offsets are 64-bit.
+// One thread moves one 16-byte chunk of two (token, kv head) rows of K and
+// of V: C = row bytes / 16 consecutive threads cover a row, and a block
+// covers 256 / C rows, then the next 256 / C.  The new rows are read exactly
+// once, so their loads are non-temporal (measured faster than plain loads);
+// the stores stay cached, since attention reads the rows back right after.
+// Indices are 32-bit (rows = tokens x heads <= 2^30); pool offsets are 64-bit.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint4 load_stream16(const char* p) {
@@ -29,31 +29,49 @@ __device__ __forceinline__ uint4 load_stream16(const char* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+constexpr int kWriteRows = 2;  // rows per thread (measured 7 % faster than one at 8,946 tokens)
+
 template <int C>
 __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a, int rows) {
-  const int r = blockIdx.x * (256 / C) + threadIdx.x / C;
+  constexpr int RB = 256 / C;  // rows of a block per pass
   const int c = threadIdx.x % C;
-  if (r >= rows) return;
-  const int eb = C / 8;  // element bytes: 16 chunks of 8 bf16, 32 chunks of 4 fp32
-  const int t = r / a.num_kv_heads;
-  const int g = r - t * a.num_kv_heads;
-  // The row loads do not depend on the slot: they are issued with the slot
-  // load, so the two memory latencies overlap (a skipped token's row is read
-  // and dropped).
-  int32_t slot = a.slots[t];
-  const uint4 kv = load_stream16(static_cast<const char*>(a.k) +
-                                 ((int64_t)t * a.k_stride + (int64_t)g * kHeadDim) * eb + c * 16);
-  const uint4 vv = load_stream16(static_cast<const char*>(a.v) +
-                                 ((int64_t)t * a.v_stride + (int64_t)g * kHeadDim) * eb + c * 16);
-  // keep the row loads ahead of the branch (the compiler would sink them into it)
-  asm volatile("" : "+v"(slot) : "v"(kv.x), "v"(kv.y), "v"(kv.z), "v"(kv.w), "v"(vv.x), "v"(vv.y),
-               "v"(vv.z), "v"(vv.w));
-  const int64_t page = slot >> a.log2_page;
-  if (slot < 0 || page >= a.num_pages) return;  // -1 = skip; out-of-range never touched
-  const int64_t off = slot & ((1 << a.log2_page) - 1);
-  const int64_t dst = ((((page * a.num_kv_heads + g) << a.log2_page) + off) * kHeadDim) * eb + c * 16;
-  *reinterpret_cast<uint4*>(static_cast<char*>(a.k_cache) + dst) = kv;
-  *reinterpret_cast<uint4*>(static_cast<char*>(a.v_cache) + dst) = vv;
+  const int eb = C / 8;        // element bytes: 16 chunks of 8 bf16, 32 chunks of 4 fp32
+  int row[kWriteRows], g[kWriteRows];
+  int32_t slot[kWriteRows];
+  uint4 kv[kWriteRows], vv[kWriteRows];
+  // The row loads do not depend on the slots: all of them are issued with
+  // the slot loads, so their memory latencies overlap (a skipped token's row
+  // is read and dropped; a row past the end re-reads the last one).
+#pragma unroll
+  for (int i = 0; i < kWriteRows; ++i) {
+    row[i] = blockIdx.x * (kWriteRows * RB) + i * RB + threadIdx.x / C;
+    const int r = row[i] < rows ? row[i] : rows - 1;
+    const int t = r / a.num_kv_heads;
+    g[i] = r - t * a.num_kv_heads;
+    slot[i] = a.slots[t];
+    kv[i] = load_stream16(static_cast<const char*>(a.k) +
+                          ((int64_t)t * a.k_stride + (int64_t)g[i] * kHeadDim) * eb + c * 16);
+    vv[i] = load_stream16(static_cast<const char*>(a.v) +
+                          ((int64_t)t * a.v_stride + (int64_t)g[i] * kHeadDim) * eb + c * 16);
+  }
+  static_assert(kWriteRows == 2, "the barrier below lists two rows");
+  // keep the row loads ahead of the branches (the compiler would sink them into them)
+  asm volatile("" : "+v"(slot[0]), "+v"(slot[1])
+               : "v"(kv[0].x), "v"(kv[0].y), "v"(kv[0].z), "v"(kv[0].w), "v"(vv[0].x),
+                 "v"(vv[0].y), "v"(vv[0].z), "v"(vv[0].w), "v"(kv[1].x), "v"(kv[1].y),
+                 "v"(kv[1].z), "v"(kv[1].w), "v"(vv[1].x), "v"(vv[1].y), "v"(vv[1].z),
+                 "v"(vv[1].w));
+#pragma unroll
+  for (int i = 0; i < kWriteRows; ++i) {
+    const int64_t page = slot[i] >> a.log2_page;
+    // past the end, -1 = skip; out-of-range slots are never touched
+    if (row[i] >= rows || slot[i] < 0 || page >= a.num_pages) continue;
+    const int64_t off = slot[i] & ((1 << a.log2_page) - 1);
+    const int64_t dst =
+        ((((page * a.num_kv_heads + g[i]) << a.log2_page) + off) * kHeadDim) * eb + c * 16;
+    *reinterpret_cast<uint4*>(static_cast<char*>(a.k_cache) + dst) = kv[i];
+    *reinterpret_cast<uint4*>(static_cast<char*>(a.v_cache) + dst) = vv[i];
+  }
 }
 
 // Fused path (bf16).  Sixteen lanes own one head row: lane j holds elements
@@ -179,11 +197,11 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float* table, int32_t m
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t s) {
   const int rows = a.num_tokens * a.num_kv_heads;
   if (a.elem_bytes == 2) {
-    const int per_block = 256 / 16;
+    const int per_block = kWriteRows * 256 / 16;
     hipLaunchKernelGGL(kv_write_kernel<16>, dim3((rows + per_block - 1) / per_block), dim3(256), 0, s,
                        a, rows);
   } else {
-    const int per_block = 256 / 32;
+    const int per_block = kWriteRows * 256 / 32;
     hipLaunchKernelGGL(kv_write_kernel<32>, dim3((rows + per_block - 1) / per_block), dim3(256), 0, s,
                        a, rows);
   }
