@@ -128,27 +128,6 @@ __device__ __forceinline__ void prefill_range(const PrefillArgs& a, int g, int r
   const bool row_valid = tok < tvalid;
   const int my_pos = prefix + t0 + min(tok, tvalid - 1);
 
-  bf16x8_t qreg[8];
-  {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                           ((int64_t)(q0 + t0 + tok) * Hq + g * G + hh) * kHeadDim;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      uint4 x = row_valid ? *reinterpret_cast<const uint4*>(qrow + 16 * t + 8 * hf)
-                          : make_uint4(0, 0, 0, 0);
-      qreg[t] = __builtin_bit_cast(bf16x8_t, x);
-    }
-  }
-
-
-  // Rows past the context are never loaded; what they hold stands in for
-  // them (their scores are masked, so their weight is exactly 0) and only has
-  // to be finite: start from zeros.
-  {
-    uint4* zf = reinterpret_cast<uint4*>(&smem[0][0][0]);
-    for (int i = tid; i < (int)(sizeof(PrefillLds) / 16); i += kThreads) zf[i] = make_uint4(0, 0, 0, 0);
-  }
-
   // Loader role.  Wavefront w fills rows 8w .. 8w+7 of the K and V tiles,
   // 4 rows (1 KB) per instruction: lane l lands at byte 16 l of that KB,
   // i.e. row 4m + l/16, physical chunk l%16, so it fetches the logical chunk
@@ -166,6 +145,33 @@ __device__ __forceinline__ void prefill_range(const PrefillArgs& a, int g, int r
     const int key = (base + lane) * kBN + kRowsPerWave * w;
     page_lane = key < L ? bt_row[key >> a.log2_page] : -1;
   };
+
+  // The first page ids go out before the query rows, and both without a
+  // branch (a row past the tile's tokens loads the last token's row and
+  // zeroes it), so the first tile's loads wait only for the page ids while
+  // the query loads are still in flight.
+  fetch_pages(kt0 & ~63);
+
+  bf16x8_t qreg[8];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                           ((int64_t)(q0 + t0 + min(tok, tvalid - 1)) * Hq + g * G + hh) * kHeadDim;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      uint4 x = *reinterpret_cast<const uint4*>(qrow + 16 * t + 8 * hf);
+      if (!row_valid) x = make_uint4(0, 0, 0, 0);
+      qreg[t] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  }
+
+
+  // Rows past the context are never loaded; what they hold stands in for
+  // them (their scores are masked, so their weight is exactly 0) and only has
+  // to be finite: start from zeros.
+  {
+    uint4* zf = reinterpret_cast<uint4*>(&smem[0][0][0]);
+    for (int i = tid; i < (int)(sizeof(PrefillLds) / 16); i += kThreads) zf[i] = make_uint4(0, 0, 0, 0);
+  }
 
   auto issue_tile = [&](int kt, int buf) __attribute__((always_inline)) {
     const int page = __builtin_amdgcn_readlane(page_lane, kt & 63);
@@ -339,7 +345,6 @@ __device__ __forceinline__ void prefill_range(const PrefillArgs& a, int g, int r
     __syncthreads();
   };
   if (kt0 < ntiles) {
-    fetch_pages(kt0 & ~63);
     __syncthreads();  // the zero fill is complete before any load lands
     issue_tile(kt0, 0);
     __builtin_amdgcn_s_waitcnt(0);
