@@ -288,10 +288,14 @@ int qil_paged_decode_append(void* out, const void* q, const void* k_new, const v
  * ("nano-vLLM learning note", Attention.forward prefill branch with cached
  * prefix and prepare_prefill: positions start at num_cached_tokens;
  * "qwen-engine" README: flat varlen prefill packed by cu_seqlens, compute-bound).
- * bf16 only (QIL_BF16); QK^T and PV run on bf16 matrix cores with fp32
+ * bf16 (QIL_BF16): QK^T and PV run on bf16 matrix cores with fp32
  * accumulation, the softmax weights are rounded to bf16 for the PV product.
+ * fp32 (QIL_F32, a tight-tolerance path): each new token runs as one row of the
+ * fp32 decode kernel over its own visible keys, on the vector ALUs; contexts up
+ * to 4,096 keys, GQA groups up to 8, at most 65,535 tokens (else
+ * QIL_EUNSUPPORTED); keys_per_split and the workspace are not used.
  *
- *   out, q         [total_q][num_q_heads][head_dim] bf16, packed by cu_seqlens_q
+ *   out, q         [total_q][num_q_heads][head_dim] (dtype), packed by cu_seqlens_q
  *   cu_seqlens_q   int32 [batch+1], cu[0] = 0, non-decreasing, cu[batch] = total_q;
  *                  request r owns rows cu[r] .. cu[r+1]-1 (n_r = cu[r+1]-cu[r] new tokens)
  *   context_lens   int32 [batch]: keys of request r including its n_r new tokens

@@ -414,9 +414,19 @@ int prep_prefill(void* out, const void* q, const void* k_cache, const void* v_ca
   *empty = false;
   if (batch < 0 || total_q < 0 || max_seqlen_q < 0)
     return fail(QIL_EINVAL, "negative batch / total_q / max_seqlen_q");
-  if (dtype != QIL_BF16) return fail(QIL_EUNSUPPORTED, "prefill is built for bf16 only");
+  if (dtype != QIL_BF16 && dtype != QIL_F32) return fail(QIL_EUNSUPPORTED, "dtype %d", dtype);
   int rc = check_common(num_q_heads, num_kv_heads, head_dim, page_size, num_pages);
   if (rc) return rc;
+  if (dtype == QIL_F32) {
+    // the fp32 path runs one query token per workgroup row on the fp32
+    // decode kernel, one split per token
+    if (num_q_heads / num_kv_heads > 8)
+      return fail(QIL_EUNSUPPORTED, "fp32 prefill is built for GQA group sizes up to 8");
+    if (max_context_len > kMaxKeysPerSplit)
+      return fail(QIL_EUNSUPPORTED, "fp32 prefill is built for contexts up to %d keys",
+                  kMaxKeysPerSplit);
+    if (total_q > 65535) return fail(QIL_EUNSUPPORTED, "fp32 prefill takes at most 65535 tokens");
+  }
   if (batch == 0 || total_q == 0 || max_seqlen_q == 0) {
     *empty = true;
     return ok();
@@ -758,13 +768,44 @@ int qil_paged_prefill(void* out, const void* q, const void* k_cache, const void*
                         context_lens, batch, total_q, max_seqlen_q, max_context_len, num_q_heads,
                         num_kv_heads, head_dim, page_size, num_pages, scale, dtype, a, &empty);
   if (rc || empty) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == QIL_F32) {
+    if (debug_on()) {
+      rc = run_checks(s, [&](qil::DebugReport* rep) { return check_prefill_metadata(a, rep, s); });
+      if (rc) return rc;
+    }
+    // each new token is a decode row over its own visible keys: no split,
+    // no workspace
+    qil::DecodeArgs d{};
+    d.out = out;
+    d.q = q;
+    d.k_cache = k_cache;
+    d.v_cache = v_cache;
+    d.block_tables = block_tables;
+    d.bt_stride = block_table_stride;
+    d.context_lens = context_lens;
+    d.batch = total_q;
+    d.num_q_heads = num_q_heads;
+    d.num_kv_heads = num_kv_heads;
+    d.log2_page = a.log2_page;
+    d.num_pages = num_pages;
+    d.max_context_len = max_context_len;
+    d.scale = scale;
+    d.keys_per_split = (max_context_len + 63) / 64 * 64;
+    d.num_splits = 1;
+    d.bf16 = false;
+    d.cu_seqlens = cu_seqlens_q;
+    d.prefill_requests = batch;
+    hipError_t e = qil::launch_decode(d, s);
+    if (e != hipSuccess) return fail(QIL_EHIP, "prefill launch: %s", hipGetErrorString(e));
+    return ok();
+  }
   const PrefillPlan plan = plan_prefill(batch, total_q, max_seqlen_q, max_context_len,
                                         num_q_heads, num_kv_heads, keys_per_split);
   const size_t need = prefill_workspace_bytes(plan, num_kv_heads);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return fail(QIL_EWORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
-  hipStream_t s = static_cast<hipStream_t>(stream);
   if (debug_on()) {
     rc = run_checks(s, [&](qil::DebugReport* rep) { return check_prefill_metadata(a, rep, s); });
     if (rc) return rc;

@@ -73,8 +73,25 @@ template <int G>
 __global__ __launch_bounds__(64 * kFW) void decode_f32_kernel(DecodeArgs a) {
   const int split = blockIdx.x;
   const int g = blockIdx.y;
-  const int r = a.order != nullptr ? a.order[blockIdx.z] : (int)blockIdx.z;
-  const int L = min(a.context_lens[r], a.max_context_len);
+  // z: the q / out row; r: the request whose block table and context it reads
+  const int z = a.order != nullptr ? a.order[blockIdx.z] : (int)blockIdx.z;
+  int r = z, L;
+  if (a.cu_seqlens != nullptr) {
+    // fp32 prefill: the last request whose rows start at or before z owns it
+    // (cu_seqlens is non-decreasing, so empty requests are passed over)
+    int lo = 0, hi = a.prefill_requests;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.cu_seqlens[mid] <= z) lo = mid;
+      else hi = mid;
+    }
+    r = lo;
+    const int n = a.cu_seqlens[r + 1] - a.cu_seqlens[r];
+    L = min(min(a.context_lens[r], a.max_context_len) - n + (z - a.cu_seqlens[r]) + 1,
+            a.max_context_len);
+  } else {
+    L = min(a.context_lens[r], a.max_context_len);
+  }
   const int kbeg = split * a.keys_per_split;
   if (kbeg >= L) return;  // this split lies past the context (uniform per block)
   const int kend = min(L, kbeg + a.keys_per_split);
@@ -92,7 +109,7 @@ __global__ __launch_bounds__(64 * kFW) void decode_f32_kernel(DecodeArgs a) {
   float qf[G][8];
   {
     const char* qbase = static_cast<const char*>(a.q) +
-                        ((int64_t)r * a.num_q_heads + (int64_t)g * G) * row_bytes;
+                        ((int64_t)z * a.num_q_heads + (int64_t)g * G) * row_bytes;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const char* qr = qbase + h * row_bytes;
@@ -262,9 +279,9 @@ __global__ __launch_bounds__(64 * kFW) void decode_f32_kernel(DecodeArgs a) {
     const int qh = g * G + h;
     if (single) {
       const float val = lsum > 0.f ? acc / lsum : 0.f;
-      static_cast<float*>(a.out)[((int64_t)r * a.num_q_heads + qh) * kHeadDim + d] = val;
+      static_cast<float*>(a.out)[((int64_t)z * a.num_q_heads + qh) * kHeadDim + d] = val;
     } else {
-      const int64_t pi = ((int64_t)r * a.num_q_heads + qh) * a.num_splits + split;
+      const int64_t pi = ((int64_t)z * a.num_q_heads + qh) * a.num_splits + split;
       a.ws_o[pi * kHeadDim + d] = acc;
       if (d == 0) {
         a.ws_m[pi] = mx;

@@ -107,6 +107,13 @@ struct DecodeArgs {
   int64_t k_new_stride;
   int64_t v_new_stride;
   const int32_t* new_slots;
+  // fp32 prefill on the fp32 decode kernel (null = decode): grid row z is new
+  // token z of the packed batch (q and out rows z), its request r is found in
+  // cu_seqlens [prefill_requests + 1], and it attends to keys 0 .. its
+  // position context_lens[r] - n_r + (z - cu_seqlens[r]) through r's block
+  // table row.
+  const int32_t* cu_seqlens;
+  int32_t prefill_requests;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);

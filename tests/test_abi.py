@@ -157,7 +157,12 @@ def pre(lib, **kw):
 def test_prefill_validation(lib):
     assert pre(lib, B=0) == 0
     assert pre(lib, T=0) == 0
-    assert pre(lib, dtype=0) == EUNSUP              # bf16 only
+    assert pre(lib, dtype=2) == EUNSUP              # no such dtype
+    # fp32 runs on the fp32 decode kernel: contexts up to 4,096 keys, G <= 8,
+    # at most 65,535 tokens
+    assert pre(lib, dtype=0, maxL=5000, bts=400) == EUNSUP
+    assert pre(lib, dtype=0, hq=32, hkv=2) == EUNSUP
+    assert pre(lib, dtype=0, T=70000) == EUNSUP
     assert pre(lib, maxq=9000) == EINVAL            # above total_q
     assert pre(lib, maxL=100) == EINVAL             # below max_seqlen_q
     assert pre(lib, maxL=200 * 16 + 1) == EINVAL

@@ -125,3 +125,39 @@ def test_max_jump_inside_a_tile(qil, hq, cached):
     ref = H.OracleCase(w, d, [0]).attention([0])
     print(f"spiked prefill hq={hq} cached={cached} max abs err", np.max(np.abs(got - ref)), flush=True)
     assert H.excess(got, ref, "bf16") <= 0
+
+
+@pytest.mark.parametrize("hq,hkv,page", [(16, 8, 16), (32, 8, 16), (8, 8, 64), (64, 8, 32), (16, 2, 256)])
+def test_fp32_ragged(qil, hq, hkv, page):
+    # fp32 prefill (the fp32 decode kernel, one row per new token) at the fp32 bar
+    ctx = [1, 65, 200, 129, 700, 33, 4000]
+    new = [1, 1, 200, 64, 131, 17, 300]
+    w = make_custom(ctx, new, hq=hq, hkv=hkv, page=page, dtype="f32", seed=hq + page + 3)
+    case = H.DeviceCase(w, DEV)
+    got = H.to_f64(case.prefill())
+    ref = H.OracleCase(w, case.data, range(w.batch)).attention(range(w.batch))
+    print(f"fp32 prefill hq={hq} hkv={hkv} page={page} max abs err", np.max(np.abs(got - ref)),
+          flush=True)
+    assert H.excess(got, ref, "f32") <= 0
+
+
+def test_fp32_decode_equals_prefill_and_chunking(qil):
+    # one query token per request: prefill rows equal decode rows (one split
+    # each); a prompt as one chunk equals the same prompt in irregular chunks
+    w = make_custom([1, 17, 300, 1024, 77], [1] * 5, page=16, dtype="f32", seed=27, decode=True)
+    case = H.DeviceCase(w, DEV)
+    dec = H.to_bits(case.decode(keys_per_split=1024))
+    pre = H.to_bits(case.prefill(requests=np.arange(5)))
+    assert np.array_equal(dec, pre)
+    L = 777
+    w = make_custom([L], [L], page=16, dtype="f32", seed=28)
+    case = H.DeviceCase(w, DEV)
+    full = H.to_bits(case.prefill())
+    parts = []
+    for a, b in [(0, 100), (100, 101), (101, L)]:
+        q = case.q_all[a:b].contiguous()
+        out = torch.empty_like(q)
+        qil.paged_prefill(out, q, case.kp, case.vp, case.bt, H.i32([0, b - a], DEV),
+                          H.i32([b], DEV), b - a, b, float(w.scale))
+        parts.append(H.to_bits(out))
+    assert np.array_equal(np.concatenate(parts), full)
