@@ -2,8 +2,9 @@
 longest first, merged by the log-sum-exp rule) against the oracle: forced
 splits over ragged varlen batches and every GQA group size, the automatic
 split of a chunk over a long prefix, the 8B-shaped mixed step's prefill
-split on request, the bit-exact indexing probe, page-permutation invariance and
-run-twice determinism."""
+split on request, the bit-exact indexing probe, page-permutation invariance, run-twice
+determinism, workspace reuse, empty requests, and replay under HIP-graph
+capture."""
 
 import numpy as np
 import pytest
@@ -165,3 +166,43 @@ def test_split_with_zero_length_and_tiny_requests(qil):
                           keys_per_split=kps)
         ref = H.OracleCase(w, case.data, keep).attention(keep)
         assert H.excess(H.to_f64(out), ref, "bf16") <= 0
+
+
+def test_split_prefill_under_graph_capture(qil):
+    # the split path (plan, pieces, merge: no memset, no host synchronisation)
+    # captured into a HIP graph: every replay equals the eager call bit for
+    # bit, with eager work and synchronisations between the replays
+    w = make_custom([4608, 2000], [512, 300], hq=32, hkv=8, page=16, seed=95)
+    case = H.DeviceCase(w, DEV)
+    reqs = np.arange(w.batch)
+    q = case.q_all
+    cu = H.i32(w.cu_seqlens(reqs), DEV)
+    maxq, maxk = int(w.new_lens.max()), int(w.context_lens.max())
+    need = qil.paged_prefill_workspace_size(w.batch, int(q.shape[0]), maxq, maxk, 32, 8, 0)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    ref = torch.empty_like(q)
+    qil.paged_prefill(ref, q, case.kp, case.vp, case.bt, cu, case.ctx, maxq, maxk, float(w.scale),
+                      workspace=ws)
+    torch.cuda.synchronize()
+    out = torch.zeros_like(q)
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        qil.paged_prefill(out, q, case.kp, case.vp, case.bt, cu, case.ctx, maxq, maxk,
+                          float(w.scale), workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qil.paged_prefill(out, q, case.kp, case.vp, case.bt, cu, case.ctx, maxq, maxk,
+                          float(w.scale), workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(H.to_bits(out), H.to_bits(ref)), f"replay {rep}"
+        x = torch.randn(1 << 20, device=DEV)
+        _ = (x * 2).sum().item()
+        torch.cuda.synchronize()
