@@ -1,10 +1,10 @@
-"""qil_paged_prefill with query tiles split over their keys (pieces ordered
-longest first, merged by the log-sum-exp rule) against the oracle: forced
-splits over ragged varlen batches and every GQA group size, the automatic
-split of a chunk over a long prefix, the 8B-shaped mixed step's prefill
-split on request, the bit-exact indexing probe, page-permutation invariance, run-twice
-determinism, workspace reuse, empty requests, and replay under HIP-graph
-capture."""
+"""qil_paged_prefill with query tiles split over their keys (pieces listed by
+a planning kernel, merged by the log-sum-exp rule) against the oracle:
+forced splits over ragged varlen batches and every GQA group size, the
+automatic split of a chunk over a long prefix, the 8B-shaped mixed step's
+prefill split on request, the bit-exact indexing probe, page-permutation
+invariance, run-twice determinism, workspace reuse, empty requests, and
+replay under HIP-graph capture."""
 
 import numpy as np
 import pytest
