@@ -45,9 +45,20 @@ def common_flags():
     ]
 
 
+# Per-source extra flags.  prefill.hip: LLVM's max-ILP machine scheduler
+# interleaves the tile loop's exponentials and conversions with its MFMAs
+# better than the default; measured side by side (same binary otherwise,
+# bit-identical outputs): prefill-varlen 121.9 -> 119.5 us, the 8B step's
+# prefill 129.6 -> 124.0 us.
+EXTRA_FLAGS = {
+    "prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *common_flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+           "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(ln for ln in (p.stderr or "").splitlines() if noise not in ln)
