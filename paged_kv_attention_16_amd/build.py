@@ -49,9 +49,12 @@ def common_flags():
 # interleaves the tile loop's exponentials and conversions with its MFMAs
 # better than the default; measured side by side (same binary otherwise,
 # bit-identical outputs): prefill-varlen 121.9 -> 119.5 us, the 8B step's
-# prefill 129.6 -> 124.0 us.
+# prefill 129.6 -> 124.0 us.  mixed.hip (the one-launch step, whose prefill
+# tiles run the same tile code): 322 -> 315 us per layer of the 8B step.
+# decode.hip measured slower with it (165.1 -> 167.3 us at 256 requests).
 EXTRA_FLAGS = {
     "prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "mixed.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
 
 
