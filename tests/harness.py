@@ -148,10 +148,9 @@ class OracleCase:
         outs = []
         for r in requests:
             n0, n1 = self.off_n[r], self.off_n[r + 1]
-            res = o_attn.paged_attention(self.q[n0:n1], self.kp, self.vp, w.block_tables[r:r + 1],
-                                         np.array([0, n1 - n0]), w.context_lens[r:r + 1],
-                                         w.scale, w.page_size, w.dtype)
-            outs.append(res)
+            outs.append(o_attn.paged_attention(self.q[n0:n1], self.kp, self.vp, w.block_tables[r:r + 1],
+                                               np.array([0, n1 - n0]), w.context_lens[r:r + 1],
+                                               w.scale, w.page_size, w.dtype))
         return np.concatenate(outs, axis=0)
 
 

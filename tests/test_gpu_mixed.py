@@ -61,9 +61,9 @@ def test_mixed_step_8b_layer(qil):
     sep_d, sep_p = separate(qil, w, case, dec, pre)
     assert np.array_equal(H.to_bits(pre["out"]), H.to_bits(sep_p))
     assert np.max(np.abs(H.to_f64(dec["out"]) - H.to_f64(sep_d))) < 1e-2
-    dsel = list(range(0, 64, 7))
+    dsel = list(range(64))
     ref = H.OracleCase(w, case.data, dsel).attention(dsel)
-    got = H.to_f64(dec["out"])[dsel]
+    got = H.to_f64(dec["out"])
     print("mixed decode max err", np.max(np.abs(got - ref)), flush=True)
     assert H.excess(got, ref, "bf16") <= 0
 
