@@ -184,6 +184,73 @@ def _token_stride(x, row):
     raise QilError(1, "expected [tokens, heads, head_dim] or [tokens, heads*head_dim]")
 
 
+def _need(cond, msg):
+    if not cond:
+        raise QilError(1, msg)
+
+
+def _tensor(t, name, dtype=None, dims=None, contiguous=False, like=None):
+    """Argument checks the C ABI cannot make on raw pointers: element type,
+    rank, contiguity, and the device of the pools (`like`)."""
+    import torch
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
+    if dtype is not None:
+        want = (dtype,) if not isinstance(dtype, tuple) else dtype
+        _need(t.dtype in want, f"{name} has dtype {t.dtype}, expected {' or '.join(map(str, want))}")
+    if dims is not None:
+        _need(t.dim() == dims, f"{name} must have {dims} dimensions, not {t.dim()}")
+    if contiguous:
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+    if like is not None:
+        _need(t.device == like.device, f"{name} is on {t.device}, the pools on {like.device}")
+    return t
+
+
+def _pools(k_cache, v_cache):
+    """Both pools: same dtype (bf16 or fp32), shape [pages, Hkv, page, 128],
+    contiguous, on one GPU."""
+    import torch
+    _tensor(k_cache, "k_cache", (torch.bfloat16, torch.float32), 4, True)
+    _tensor(v_cache, "v_cache", k_cache.dtype, 4, True, like=k_cache)
+    _need(tuple(v_cache.shape) == tuple(k_cache.shape), "k_cache and v_cache shapes differ")
+    return _pool_shape(k_cache)
+
+
+def _on_gpu(pool):
+    """Last check before a library call: the tensors (all on the pools'
+    device by the checks above) are GPU memory."""
+    _need(pool.is_cuda, "the pools (and every tensor argument) must be GPU tensors")
+
+
+def _i32(t, name, like, length=None, dims=1):
+    import torch
+    _tensor(t, name, torch.int32, dims, True, like=like)
+    if length is not None:
+        _need(int(t.shape[0]) == length, f"{name} has {int(t.shape[0])} entries, expected {length}")
+    return t
+
+
+def _rows(q, out, name_q, name_out, pool, hq=None):
+    """q and out: [rows, Hq, 128] in the pool dtype, contiguous, same shape."""
+    _tensor(q, name_q, pool.dtype, 3, True, like=pool)
+    _tensor(out, name_out, pool.dtype, 3, True, like=pool)
+    _need(tuple(out.shape) == tuple(q.shape), f"{name_out} shape {tuple(out.shape)} differs from "
+          f"{name_q} shape {tuple(q.shape)}")
+    _need(int(q.shape[2]) == int(pool.shape[3]), f"{name_q} head_dim differs from the pools'")
+
+
+def _new_rows(x, name, pool):
+    """k/v rows to write: pool dtype, [T, Hkv, 128] or row views with a token stride."""
+    _tensor(x, name, pool.dtype, like=pool)
+    _need(x.dim() in (2, 3), f"{name} must be [tokens, heads, head_dim] or [tokens, heads*head_dim]")
+
+
+def _workspace(ws, like):
+    if ws is not None:
+        import torch
+        _tensor(ws, "workspace", torch.uint8, 1, True, like=like)
+
+
 class QKNormRope:
     """Parameters of the fused Q/K RMSNorm + RoPE write (bf16)."""
 
@@ -193,6 +260,16 @@ class QKNormRope:
         self.q_norm_weight, self.k_norm_weight = q_norm_weight, k_norm_weight
         self.positions, self.cos_sin, self.eps = positions, cos_sin, float(eps)
         self.num_q_heads = int(num_q_heads if num_q_heads is not None else q.shape[1])
+
+    def check(self, pool):
+        import torch
+        _tensor(self.q, "fuse.q", torch.bfloat16, like=pool)
+        _need(self.q.dim() in (2, 3), "fuse.q must be [tokens, heads, head_dim] or a row view")
+        _tensor(self.q_out, "fuse.q_out", torch.bfloat16, 3, True, like=pool)
+        _tensor(self.q_norm_weight, "fuse.q_norm_weight", torch.bfloat16, 1, True, like=pool)
+        _tensor(self.k_norm_weight, "fuse.k_norm_weight", torch.bfloat16, 1, True, like=pool)
+        _i32(self.positions, "fuse.positions", pool)
+        _tensor(self.cos_sin, "fuse.cos_sin", torch.float32, 2, True, like=pool)
 
     def as_c(self, head_dim):
         return _QKNormRopeC(
@@ -204,10 +281,16 @@ class QKNormRope:
 def kv_write(k, v, k_cache, v_cache, slot_mapping, fuse=None, stream=None):
     """Scatter k, v ([T, Hkv, 128] or row views with a token stride) into the
     pools through slot_mapping (int32 [T], -1 = skip)."""
-    num_pages, hkv, page, d = _pool_shape(k_cache)
+    num_pages, hkv, page, d = _pools(k_cache, v_cache)
+    _new_rows(k, "k", k_cache)
+    _new_rows(v, "v", k_cache)
+    _i32(slot_mapping, "slot_mapping", k_cache, int(k.shape[0]))
     c_fuse = None
     if fuse is not None:
+        fuse.check(k_cache)
+        _need(int(fuse.positions.shape[0]) == int(k.shape[0]), "fuse.positions must have one entry per token")
         c_fuse = ctypes.pointer(fuse.as_c(d))
+    _on_gpu(k_cache)
     rc = load().qil_kv_write(
         _ptr(k), _ptr(v), _token_stride(k, hkv * d), _token_stride(v, hkv * d),
         _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), int(slot_mapping.shape[0]), hkv, d,
@@ -228,13 +311,27 @@ def qkv_proj_write(x, weight, k_cache, v_cache, slot_mapping, q_out, num_q_heads
     rotated k and projected v rows into the pools through slot_mapping.
     qkv_out ([T, (Hq + 2 Hkv) * 128]) optionally receives the rounded
     projection."""
-    num_pages, hkv, page, d = _pool_shape(k_cache)
-    if x.dim() != 2 or weight.dim() != 2 or x.stride(1) != 1 or weight.stride(1) != 1:
+    import torch
+    num_pages, hkv, page, d = _pools(k_cache, v_cache)
+    _tensor(x, "x", torch.bfloat16, 2, like=k_cache)
+    _tensor(weight, "weight", torch.bfloat16, 2, like=k_cache)
+    if x.stride(1) != 1 or weight.stride(1) != 1:
         raise QilError(1, "x and weight must be 2-D with contiguous rows")
+    _tensor(q_out, "q_out", torch.bfloat16, 3, True, like=k_cache)
+    _need(tuple(q_out.shape) == (int(x.shape[0]), int(num_q_heads), d),
+          f"q_out must be [{int(x.shape[0])}, {int(num_q_heads)}, {d}]")
+    if qkv_out is not None:
+        _tensor(qkv_out, "qkv_out", torch.bfloat16, 2, True, like=k_cache)
+    _i32(slot_mapping, "slot_mapping", k_cache, int(x.shape[0]))
+    _i32(positions, "positions", k_cache, int(x.shape[0]))
+    _tensor(q_norm_weight, "q_norm_weight", torch.bfloat16, 1, True, like=k_cache)
+    _tensor(k_norm_weight, "k_norm_weight", torch.bfloat16, 1, True, like=k_cache)
+    _tensor(cos_sin, "cos_sin", torch.float32, 2, True, like=k_cache)
+    _workspace(workspace, k_cache)
     hidden = int(x.shape[1])
     if int(weight.shape[1]) != hidden or int(weight.shape[0]) != (num_q_heads + 2 * hkv) * d:
         raise QilError(1, f"weight must be [{(num_q_heads + 2 * hkv) * d}, {hidden}]")
-    import torch
+    _on_gpu(k_cache)
     need = qkv_proj_workspace_size(int(x.shape[0]), int(num_q_heads), hkv, hidden)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
@@ -250,6 +347,9 @@ def qkv_proj_write(x, weight, k_cache, v_cache, slot_mapping, q_out, num_q_heads
 
 def rope_cos_sin(table, theta, stream=None):
     """Fill an fp32 [max_position, 128] tensor with the cos/sin table."""
+    import torch
+    _tensor(table, "table", torch.float32, 2, True)
+    _need(table.is_cuda, "table must be a GPU tensor")
     rc = load().qil_rope_cos_sin(_ptr(table), int(table.shape[0]), int(table.shape[1]),
                                  float(theta), _stream(stream))
     _check(rc)
@@ -265,8 +365,13 @@ def paged_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_conte
                  keys_per_split=0, workspace=None, stream=None):
     """out, q: [B, Hq, 128]; block_tables int32 [B, stride]; context_lens int32 [B]."""
     import torch
-    num_pages, hkv, page, d = _pool_shape(k_cache)
+    num_pages, hkv, page, d = _pools(k_cache, v_cache)
+    _rows(q, out, "q", "out", k_cache)
     batch, hq = int(q.shape[0]), int(q.shape[1])
+    _i32(block_tables, "block_tables", k_cache, batch, dims=2)
+    _i32(context_lens, "context_lens", k_cache, batch)
+    _workspace(workspace, k_cache)
+    _on_gpu(k_cache)
     need = paged_decode_workspace_size(batch, hq, hkv, int(max_context_len), page, keys_per_split)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -287,8 +392,18 @@ def paged_decode_append(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, bl
     slot of each request's last position (-1: padding row); otherwise as
     paged_decode."""
     import torch
-    num_pages, hkv, page, d = _pool_shape(k_cache)
+    num_pages, hkv, page, d = _pools(k_cache, v_cache)
+    _rows(q, out, "q", "out", k_cache)
     batch, hq = int(q.shape[0]), int(q.shape[1])
+    _new_rows(k_new, "k_new", k_cache)
+    _new_rows(v_new, "v_new", k_cache)
+    _need(int(k_new.shape[0]) == batch and int(v_new.shape[0]) == batch,
+          "k_new and v_new must hold one row per request")
+    _i32(slot_mapping, "slot_mapping", k_cache, batch)
+    _i32(block_tables, "block_tables", k_cache, batch, dims=2)
+    _i32(context_lens, "context_lens", k_cache, batch)
+    _workspace(workspace, k_cache)
+    _on_gpu(k_cache)
     need = paged_decode_workspace_size(batch, hq, hkv, int(max_context_len), page, keys_per_split)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -315,9 +430,15 @@ def paged_prefill(out, q, k_cache, v_cache, block_tables, cu_seqlens_q, context_
                   stream=None):
     """out, q: [total_q, Hq, 128] bf16 packed by cu_seqlens_q (int32 [B+1])."""
     import torch
-    num_pages, hkv, page, d = _pool_shape(k_cache)
+    num_pages, hkv, page, d = _pools(k_cache, v_cache)
+    _rows(q, out, "q", "out", k_cache)
     total_q, hq = int(q.shape[0]), int(q.shape[1])
+    _i32(context_lens, "context_lens", k_cache)
     batch = int(context_lens.shape[0])
+    _i32(cu_seqlens_q, "cu_seqlens_q", k_cache, batch + 1)
+    _i32(block_tables, "block_tables", k_cache, batch, dims=2)
+    _workspace(workspace, k_cache)
+    _on_gpu(k_cache)
     need = paged_prefill_workspace_size(batch, total_q, int(max_seqlen_q), int(max_context_len),
                                         hq, hkv, keys_per_split)
     if workspace is None and need > 0:
@@ -340,9 +461,24 @@ def paged_attention_mixed(k_cache, v_cache, scale, decode=None, prefill=None, st
                   max_seqlen_q, max_context_len)      (as paged_prefill)
     """
     import torch
-    num_pages, hkv, page, d = _pool_shape(k_cache)
+    num_pages, hkv, page, d = _pools(k_cache, v_cache)
+    _need(decode is not None or prefill is not None, "give a decode batch, a prefill batch or both")
     ref_q = (decode or prefill)["q"]
     hq = int(ref_q.shape[1])
+    if decode is not None:
+        _rows(decode["q"], decode["out"], "decode q", "decode out", k_cache)
+        nb = int(decode["q"].shape[0])
+        _i32(decode["block_tables"], "decode block_tables", k_cache, nb, dims=2)
+        _i32(decode["context_lens"], "decode context_lens", k_cache, nb)
+        _workspace(decode.get("workspace"), k_cache)
+    if prefill is not None:
+        _rows(prefill["q"], prefill["out"], "prefill q", "prefill out", k_cache)
+        _need(int(prefill["q"].shape[1]) == hq, "the two batches have different head counts")
+        _i32(prefill["context_lens"], "prefill context_lens", k_cache)
+        nb = int(prefill["context_lens"].shape[0])
+        _i32(prefill["cu_seqlens_q"], "prefill cu_seqlens_q", k_cache, nb + 1)
+        _i32(prefill["block_tables"], "prefill block_tables", k_cache, nb, dims=2)
+    _on_gpu(k_cache)
     dptr = pptr = None
     keep = []
     if decode is not None:

@@ -715,7 +715,7 @@ int qil_paged_decode_append(void* out, const void* q, const void* k_new, const v
       if (e == hipSuccess) e = qil::launch_check_slots(slot_mapping, batch, num_slots, rep, s);
       if (e == hipSuccess)
         e = qil::launch_check_append(slot_mapping, block_tables, block_table_stride, context_lens,
-                                     batch, a.log2_page, rep, s);
+                                     batch, a.log2_page, num_pages, max_context_len, rep, s);
       return e;
     });
     if (rc) return rc;

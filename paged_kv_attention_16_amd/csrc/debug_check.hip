@@ -77,16 +77,23 @@ __global__ void tables_kernel(const int32_t* bt, int32_t stride, const int32_t* 
 }
 
 // Decode with append: request r's new token goes to the slot of its last
-// position, or nowhere (-1); its context already passed tables_kernel.
+// position, or nowhere (-1).  tables_kernel runs first on the same stream
+// but does not stop this kernel, so a context length outside
+// [1, min(max_context_len, stride * page_size)] (already reported there) is
+// skipped here before any block-table read, and so is a table entry that is
+// not a page of the pool (also reported there).
 __global__ void append_kernel(const int32_t* slots, const int32_t* bt, int32_t stride,
                               const int32_t* ctx, int32_t batch, int32_t log2_page,
-                              DebugReport* rep) {
+                              int32_t num_pages, int32_t max_context_len, DebugReport* rep) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= batch) return;
-  const int32_t pos = ctx[r] - 1;
-  if (pos < 0 || slots[r] == -1) return;  // -1: no pool write for this request
-  const int32_t want = (bt[(int64_t)r * stride + (pos >> log2_page)] << log2_page) +
-                       (pos & ((1 << log2_page) - 1));
+  const int32_t L = ctx[r];
+  const int64_t cap = min((int64_t)max_context_len, (int64_t)stride << log2_page);
+  if (L < 1 || (int64_t)L > cap || slots[r] == -1) return;  // -1: no pool write for this request
+  const int32_t pos = L - 1;
+  const int32_t page = bt[(int64_t)r * stride + (pos >> log2_page)];
+  if (page < 0 || page >= num_pages) return;
+  const int32_t want = (page << log2_page) + (pos & ((1 << log2_page) - 1));
   if (slots[r] != want) report(rep, kAppendSlot, r, want, slots[r]);
 }
 
@@ -163,10 +170,12 @@ hipError_t launch_check_tables(const int32_t* block_tables, int32_t bt_stride,
 
 hipError_t launch_check_append(const int32_t* slots, const int32_t* block_tables, int32_t bt_stride,
                                const int32_t* context_lens, int32_t batch, int32_t log2_page,
-                               DebugReport* rep, hipStream_t s) {
+                               int32_t num_pages, int32_t max_context_len, DebugReport* rep,
+                               hipStream_t s) {
   if (batch <= 0) return hipSuccess;
   hipLaunchKernelGGL(append_kernel, dim3((batch + 255) / 256), dim3(256), 0, s, slots,
-                     block_tables, bt_stride, context_lens, batch, log2_page, rep);
+                     block_tables, bt_stride, context_lens, batch, log2_page, num_pages,
+                     max_context_len, rep);
   return hipGetLastError();
 }
 

@@ -212,6 +212,7 @@ hipError_t launch_check_cu(const int32_t* cu, const int32_t* context_lens, int32
 // slot_mapping[r] is the slot of position context_lens[r] - 1 (decode with append)
 hipError_t launch_check_append(const int32_t* slots, const int32_t* block_tables, int32_t bt_stride,
                                const int32_t* context_lens, int32_t batch, int32_t log2_page,
-                               DebugReport* rep, hipStream_t s);
+                               int32_t num_pages, int32_t max_context_len, DebugReport* rep,
+                               hipStream_t s);
 
 }  // namespace qil

@@ -89,3 +89,27 @@ def test_debug_mode_checks_the_slot(qil):
     finally:
         qil.set_debug(False)
     torch.cuda.synchronize()
+
+
+def test_debug_mode_context_past_the_table_row(qil):
+    """A context length past its block-table row (and past max_context_len)
+    is reported as a bad context, and the slot check that runs after the
+    table check reads no block-table entry for that request (the last row of
+    the table is the one whose read would leave the table)."""
+    w = make_custom([40, 300, 17], [1, 1, 1], page=16, seed=13, decode=True)
+    app = H.DeviceCase(w, DEV, write_new=False)
+    out = torch.empty_like(app.q_all)
+    stride = int(app.bt.shape[1])
+    ctx = app.ctx.clone()
+    ctx[2] = stride * 16 + 1                    # one key past request 2's table row
+    qil.set_debug(True)
+    try:
+        # max_context_len itself may not exceed the table row (checked on the host)
+        for maxl in (int(w.context_lens.max()), stride * 16):
+            with pytest.raises(qil.QilError) as err:
+                qil.paged_decode_append(out, app.q_all, app.k_new, app.v_new, app.new_slots, app.kp,
+                                        app.vp, app.bt, ctx, maxl, float(w.scale))
+            assert err.value.code == 1 and "context_lens[2]" in str(err.value), str(err.value)
+    finally:
+        qil.set_debug(False)
+    torch.cuda.synchronize()
