@@ -225,23 +225,15 @@ def write_bytes(w, tokens):
     return tokens * w.num_kv_heads * w.head_dim * w.elem_bytes * 2 * 2 + 4 * tokens
 
 
-def gpu_legs(args):
+def decode_leg(w, args, dev, stream, flush, label):
+    """One decode workload: the step (write the batch's new tokens, then paged
+    decode over every context) as one qil_paged_decode_append call, the same
+    without the cache flush, and as two calls (qil_kv_write, then
+    qil_paged_decode).  The decode call's launch time is (flush, write,
+    decode) minus (flush, write): both steps start with the same single event
+    marker and have none between their kernels."""
     import torch
     import paged_kv_attention_16_amd as qil
-    from workloads import make_workload
-
-    if not os.path.exists(qil.lib_path()):
-        import __graft_entry__
-        __graft_entry__.build()
-    dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream()
-    flush = None if args.no_flush else torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
-    res = {}
-
-    res["ceilings"] = measured_ceilings(dev, stream)
-
-    # ---- decode leg (headline) -------------------------------------------
-    w = make_workload(3)
     t0 = time.time()
     x = Inputs(w, dev)
     torch.cuda.synchronize()
@@ -275,23 +267,46 @@ def gpu_legs(args):
     # ... and as two calls (qil_kv_write, then qil_paged_decode): the decode
     # call alone is the roofline kernel (run last, so counter runs that keep
     # the last launches of the largest decode grid see this call)
+    tw = timed_steps([write], args.steps, args.warmup, flush, stream)
     t = timed_steps([write, decode], args.steps, args.warmup, flush, stream)
     wall = time.perf_counter() - wall0
-    res["decode"] = dict(
+    dec_ms = t["step_mean"] - tw["step_mean"]
+    out = dict(
         workload=w, step_ms=tf["step_mean"], step_ms_median=tf["step_median"],
         step_ms_p10=tf["step_p10"], step_ms_p90=tf["step_p90"],
         step_bracket_ms=float(tf["mean"][0]), step_bracket_ms_median=float(tf["median"][0]),
         hot_step_ms=th["step_mean"],
-        two_call_step_ms=t["step_mean"], dec_ms=t["last_ms"], dec_bracket_ms=float(t["mean"][1]),
-        write_ms=float(t["mean"][0]),
+        two_call_step_ms=t["step_mean"], dec_ms=dec_ms, dec_bracket_ms=float(t["mean"][1]),
+        write_ms=tw["step_mean"],
         step_bytes=step_bytes, dec_bytes=dec_bytes,
         kv_bytes=kv_bytes, wall_s=wall, setup_s=setup_s, workspace=need)
-    print(f"[bench] decode-b256: one-call step {tf['step_mean']*1e3:.1f} us "
+    print(f"[bench] {label}: one-call step {tf['step_mean']*1e3:.1f} us "
           f"({step_bytes / (tf['step_mean'] * 1e-3) / 1e9:.0f} GB/s); two calls {t['step_mean']*1e3:.1f} us, "
-          f"decode {t['last_ms']*1e3:.1f} us ({dec_bytes / (t['last_ms'] * 1e-3) / 1e9:.0f} GB/s), "
-          f"setup {setup_s:.1f}s", flush=True)
+          f"write alone {tw['step_mean']*1e3:.1f} us, decode {dec_ms*1e3:.1f} us "
+          f"({dec_bytes / (dec_ms * 1e-3) / 1e9:.0f} GB/s), setup {setup_s:.1f}s", flush=True)
     del x, ws
     torch.cuda.empty_cache()
+    return out
+
+
+def gpu_legs(args):
+    import torch
+    import paged_kv_attention_16_amd as qil
+    from workloads import make_workload
+
+    if not os.path.exists(qil.lib_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    flush = None if args.no_flush else torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    res = {}
+
+    res["ceilings"] = measured_ceilings(dev, stream)
+
+    # ---- decode legs: decode-b256 (headline), then decode-b32 -------------
+    res["decode"] = decode_leg(make_workload(3), args, dev, stream, flush, "decode-b256")
+    res["decode_b32"] = decode_leg(make_workload(2), args, dev, stream, flush, "decode-b32")
 
     # ---- prefill leg ---------------------------------------------------------
     if not args.skip_prefill:
@@ -814,7 +829,7 @@ def cpu_baseline(seconds):
         nbytes += int(w.context_lens[r]) * w.num_kv_heads * w.head_dim * 2 * 2
     ru1 = resource.getrusage(resource.RUSAGE_SELF)
     cpu = (ru1.ru_utime - ru0.ru_utime) + (ru1.ru_stime - ru0.ru_stime)
-    cores = max(1, int(round(cpu / max(busy, 1e-9))))
+    cores = round(cpu / max(busy, 1e-9), 1)      # CPU time / wall time: cores busy on average
     del kp, vp
 
     w4 = make_workload(4)
@@ -861,7 +876,8 @@ def cpu_baseline(seconds):
                     if i.get("user_api") == "blas"), default=1)
     except Exception:  # the count is informational
         blas = None
-    return dict(value=nbytes / busy / 1e9, unit="GB/s", cores=cores, kind="oracle", blas_threads=blas,
+    return dict(value=nbytes / busy / 1e9, unit="GB/s", cores=len(os.sched_getaffinity(0)),
+                busy_cores_estimate=cores, kind="oracle", blas_threads=blas,
                 sample=f"decode-b256 step, all {w.batch} requests (scatter write + fp64 decode over "
                        f"{nbytes / 1e6:.0f} MB of K/V), {busy:.1f} s on the host; "
                        f"{len(os.sched_getaffinity(0))} usable cores",
@@ -884,11 +900,16 @@ KERNEL_SOURCES = {
 
 
 def sources_sha256(files):
-    """SHA-256 over the kernel's source files, in order."""
+    """SHA-256 over the kernel's source files, in order, and the compiler
+    flags of its translation unit (the first file): a flag change alone
+    also retires the traffic figures."""
+    from paged_kv_attention_16_amd import build as qbuild
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(ROOT, "paged_kv_attention_16_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+    flags = [a for a in qbuild.common_flags() if not a.startswith(os.sep) and a != "-I"]
+    h.update(" ".join(flags + qbuild.EXTRA_FLAGS.get(files[0], [])).encode())
     return h.hexdigest()
 
 
@@ -1034,8 +1055,8 @@ def main():
             "traffic": traffic_for("decode-b256"),
             "algorithmic_bytes_per_launch": int(dec["dec_bytes"]),
             "launch_us_mean": round(dec["dec_ms"] * 1e3, 2),
-            "launch_timing": "mean two-call step time with no marker between the kernels, minus the "
-                             "separately bracketed write",
+            "launch_timing": "mean time of (flush, write, decode) minus mean time of (flush, write): "
+                             "one event marker before the first kernel of each, none between kernels",
             "event_bracket_us_mean": round(dec["dec_bracket_ms"] * 1e3, 2),
             "measured_ceiling": res["ceilings"]["stream_read_GB_s"],
             "frac_of_measured": round(achieved / res["ceilings"]["stream_read_GB_s"], 4),
@@ -1053,11 +1074,27 @@ def main():
             "calls": "qil_kv_write (256 tokens) then qil_paged_decode",
             "step_us": round(dec["two_call_step_ms"] * 1e3, 2),
             "GB_per_s": round(dec["step_bytes"] / (dec["two_call_step_ms"] * 1e-3) / 1e9, 1),
-            "write_bracket_us": round(dec["write_ms"] * 1e3, 2),
+            "write_alone_us": round(dec["write_ms"] * 1e3, 2),
         },
         "step_us": {"mean": round(dec["step_ms"] * 1e3, 2), "median": round(dec["step_ms_median"] * 1e3, 2),
                     "p10": round(dec["step_ms_p10"] * 1e3, 2), "p90": round(dec["step_ms_p90"] * 1e3, 2)},
         "decode_tokens_per_s": round(w.batch / (dec["step_ms"] * 1e-3), 1),
+    }
+    d2 = res["decode_b32"]
+    a2 = d2["dec_bytes"] / (d2["dec_ms"] * 1e-3) / 1e9
+    v2 = d2["step_bytes"] / (d2["step_ms"] * 1e-3) / 1e9
+    line["decode_b32"] = {
+        "workload": "decode-b32: 32 requests, Hq 16 / Hkv 8 (Qwen3-0.6B attention), page 16, "
+                    "context U[128,2048], pool 8192 pages; step = write 32 new tokens + paged decode",
+        "bound": "hbm", "achieved": round(a2, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(a2 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_launch": int(d2["dec_bytes"]),
+        "launch_us_mean": round(d2["dec_ms"] * 1e3, 2),
+        "launch_timing": "(flush, write, decode) minus (flush, write), as for the roofline kernel",
+        "fused_step": {"us": round(d2["step_ms"] * 1e3, 2), "GB_per_s": round(v2, 1),
+                       "frac": round(v2 / HBM_PEAK_GBS, 4)},
+        "two_call_step_us": round(d2["two_call_step_ms"] * 1e3, 2),
+        "decode_tokens_per_s": round(d2["workload"].batch / (d2["step_ms"] * 1e-3), 1),
     }
     if "prefill" in res:
         p = res["prefill"]
@@ -1106,12 +1143,20 @@ def main():
             "single_launch_us": round(m["single_launch_ms"] * 1e3, 2),
             "us_per_36_layer_step": round(m["layer_ms"] * 1e3 * 36, 1),
             "tokens_per_s_36_layers": round((64 + 2048) / (m["layer_ms"] * 36 * 1e-3), 1),
+            "per_call_timing": "event brackets around each call (pass 1 of timed_steps); a bracket "
+                               "includes the dispatch gap a marker puts in front of its kernel",
             "fused_write": {"us": round(m["fused_ms"] * 1e3, 2),
-                            "GB_per_s": round(m["fused_bytes"] / (m["fused_ms"] * 1e-3) / 1e9, 1)},
+                            "GB_per_s": round(m["fused_bytes"] / (m["fused_ms"] * 1e-3) / 1e9, 1),
+                            "bound": "hbm", "peak": HBM_PEAK_GBS,
+                            "frac": round(m["fused_bytes"] / (m["fused_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
             "decode": {"us": round(m["dec_ms"] * 1e3, 2),
-                       "GB_per_s": round(m["dec_bytes"] / (m["dec_ms"] * 1e-3) / 1e9, 1)},
+                       "GB_per_s": round(m["dec_bytes"] / (m["dec_ms"] * 1e-3) / 1e9, 1),
+                       "bound": "hbm", "peak": HBM_PEAK_GBS,
+                       "frac": round(m["dec_bytes"] / (m["dec_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
             "prefill": {"us": round(m["pre_ms"] * 1e3, 2),
-                        "TFLOP_per_s": round(m["pre_flops"] / (m["pre_ms"] * 1e-3) / 1e12, 1)}}
+                        "TFLOP_per_s": round(m["pre_flops"] / (m["pre_ms"] * 1e-3) / 1e12, 1),
+                        "bound": "mfma", "peak": BF16_PEAK_TFLOPS,
+                        "frac": round(m["pre_flops"] / (m["pre_ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}}
     if "graph" in res:
         gr = res["graph"]
         line["decode_graph"] = {
