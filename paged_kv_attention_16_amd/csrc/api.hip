@@ -374,12 +374,12 @@ PrefillPlan plan_prefill(int32_t batch, int32_t total_q, int32_t max_seqlen_q,
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace of a split prefill: header, piece list, split list, then the
-// partial rows (bf16) and their (max, sum) pairs.
+// partial rows (fp32 sums) and their (max, sum) pairs.
 size_t prefill_workspace_bytes(const PrefillPlan& p, int32_t num_kv_heads) {
   if (p.S == 0) return 0;
   const size_t slabs = (size_t)p.entries * p.pieces * num_kv_heads;
   return 256 + round256((size_t)p.items * 32) + round256((size_t)p.entries * 16) +
-         round256(slabs * 256 * 128 * 2) + slabs * 256 * 2 * 4;
+         round256(slabs * 256 * 128 * 4) + slabs * 256 * 2 * 4;
 }
 
 qil::PrefillSplit prefill_split_args(const PrefillPlan& p, int32_t num_kv_heads, void* ws) {
@@ -397,8 +397,8 @@ qil::PrefillSplit prefill_split_args(const PrefillPlan& p, int32_t num_kv_heads,
   b += round256((size_t)p.items * 32);
   sp.splits = reinterpret_cast<int32_t*>(b);
   b += round256((size_t)p.entries * 16);
-  sp.part_o = reinterpret_cast<uint16_t*>(b);
-  b += round256(slabs * 256 * 128 * 2);
+  sp.part_o = reinterpret_cast<float*>(b);
+  b += round256(slabs * 256 * 128 * 4);
   sp.part_ml = reinterpret_cast<float*>(b);
   return sp;
 }

@@ -10,10 +10,10 @@
 //      so pieces over the same keys share L2, then the unsplit tiles longest
 //      first.
 //   2. prefill_piece_kernel<G> runs one piece per workgroup: whole tiles
-//      write the output, pieces of split tiles write their normalized rows
-//      and (max, sum) to the workspace.
+//      write the output, pieces of split tiles write their unnormalized fp32
+//      rows and (integer max, sum) to the workspace.
 //   3. prefill_merge_kernel combines the pieces of each split tile by the
-//      log-sum-exp rule: out = sum_p 2^(m_p - M) l_p o_p / sum_p 2^(m_p - M) l_p.
+//      log-sum-exp rule: out = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p.
 // The order of pieces within one place is arbitrary, but every piece and
 // every merge computes the same values whatever the order, so results are
 // deterministic.
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void prefill_piece_kernel(PrefillArgs a, 
   const int r = wave_uniform(i0.x), tile = wave_uniform(i0.y);
   const int kb = wave_uniform(i0.z), ke = wave_uniform(i0.w);
   const int p = wave_uniform(i1.x), j = wave_uniform(i1.z);
-  uint16_t* po = nullptr;
+  float* po = nullptr;
   float* pml = nullptr;
   if (j >= 0) {
     const int64_t slab = ((int64_t)j * sp.max_pieces + p) * a.num_kv_heads + g;
@@ -167,11 +167,19 @@ __global__ __launch_bounds__(kThreads) void prefill_piece_kernel(PrefillArgs a, 
 // One workgroup per (KV head, split tile, 8-row block); each wavefront
 // merges two rows, a 32-lane half per row.  Lane p of the half holds piece
 // p's (m, l) (at most 32 pieces), and every lane sums 4 dims of the pieces'
-// rows.  The loads of the first eight pieces are issued together with the
-// (m, l) load, before the half reduces the maximum M and the weights
-// w_p = 2^(m_p - M) l_p with lane shuffles.
+// fp32 rows.  The loads of the first eight pieces are issued together with
+// the (m, l) load, before the half reduces the maximum M and the weights
+// 2^(m_p - M) with lane shuffles.  The references m_p are integers, so each
+// weight is an exact power of two:
+//     out = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p
+// is the whole row's O / l up to the order of the fp32 additions.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeRows = 8;
+
+__device__ __forceinline__ float pow2_weight(float m, float M) {
+  // m <= M; pieces that saw no visible key keep the -1e30 start value
+  return ldexpf(1.0f, (int)fmaxf(m - M, -200.0f));
+}
 
 __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArgs a, PrefillSplit sp,
                                                                       int G) {
@@ -192,23 +200,24 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArg
   const int tok = row / G, hh = row % G;
   const bool live = tok < tvalid;  // rows past the tile's tokens hold nothing
   const int64_t ostride = (int64_t)a.num_kv_heads * kRowsWG * kHeadDim;  // between pieces
-  const uint16_t* orow = sp.part_o +
-                         ((int64_t)j * sp.max_pieces * a.num_kv_heads + g) * kRowsWG * kHeadDim +
-                         (int64_t)row * kHeadDim + 4 * hl;
+  const float* orow = sp.part_o +
+                      ((int64_t)j * sp.max_pieces * a.num_kv_heads + g) * kRowsWG * kHeadDim +
+                      (int64_t)row * kHeadDim + 4 * hl;
   const float* mlrow = sp.part_ml +
                        (((int64_t)j * a.num_kv_heads + g) * kRowsWG + row) * sp.max_pieces * 2;
-  float2 ml = make_float2(-INFINITY, 0.f);
+  float2 ml = make_float2(-1.0e30f, 0.f);
   if (hl < pcs && live) ml = *reinterpret_cast<const float2*>(mlrow + 2 * hl);
-  uint2 o[8];
+  float4 o[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k)
-    o[k] = k < pcs && live ? *reinterpret_cast<const uint2*>(orow + k * ostride) : make_uint2(0u, 0u);
+    o[k] = k < pcs && live ? *reinterpret_cast<const float4*>(orow + k * ostride)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
   // both halves run the shuffles (whole-wavefront instructions)
   float M = ml.x;
 #pragma unroll
   for (int d = 16; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d));
-  const float w = hl < pcs && live ? fast_exp2(ml.x - M) * ml.y : 0.f;
-  float lsum = w;
+  const float w = hl < pcs && live ? pow2_weight(ml.x, M) : 0.f;
+  float lsum = w * ml.y;
 #pragma unroll
   for (int d = 16; d >= 1; d >>= 1) lsum += __shfl_xor(lsum, d);
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -216,17 +225,17 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArg
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const float wp = __shfl(w, hbase + ((p0 + k) & 31));
-      acc[0] = fmaf(wp, __uint_as_float(o[k].x << 16), acc[0]);
-      acc[1] = fmaf(wp, __uint_as_float(o[k].x & 0xffff0000u), acc[1]);
-      acc[2] = fmaf(wp, __uint_as_float(o[k].y << 16), acc[2]);
-      acc[3] = fmaf(wp, __uint_as_float(o[k].y & 0xffff0000u), acc[3]);
+      acc[0] = fmaf(wp, o[k].x, acc[0]);
+      acc[1] = fmaf(wp, o[k].y, acc[1]);
+      acc[2] = fmaf(wp, o[k].z, acc[2]);
+      acc[3] = fmaf(wp, o[k].w, acc[3]);
     }
     p0 += 8;
     if (p0 >= pcs) break;
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-      o[k] = p0 + k < pcs && live ? *reinterpret_cast<const uint2*>(orow + (int64_t)(p0 + k) * ostride)
-                                  : make_uint2(0u, 0u);
+      o[k] = p0 + k < pcs && live ? *reinterpret_cast<const float4*>(orow + (int64_t)(p0 + k) * ostride)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   if (!live) return;
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;

@@ -33,7 +33,13 @@
 //     check runs once per 64-key tile, on the maximum of the whole tile and
 //     before any weight of the tile is formed, so every weight added to O
 //     and to the row sum is relative to the same reference.  The row sum
-//     adds the same rounded weights that feed the PV product.
+//     adds the same rounded weights that feed the PV product.  The
+//     reference is an integer (the ceiling of the row maximum), so a weight
+//     rounded to bf16 is the same bf16 value times a power of two whatever
+//     the reference, and a rescale multiplies by an exact power of two: the
+//     result does not depend on where the rescales fall, and pieces of one
+//     row's keys (the split over keys) merge to the whole row's sums up to
+//     the order of fp32 additions.
 //   * Causal masking only on the diagonal band of tiles.
 //   * Each 64-key tile runs as two 32-key halves: the first half's row
 //     maximum sits next to the second half's QK^T matrix work, and the first
@@ -91,14 +97,14 @@ typedef char PrefillLds[2][2][kBN * 256];
 
 // Key tiles [kt_begin, kt_end) of one query tile: KV head g, request r,
 // query tile `tile`.  With part_o null the rows are final and go to a.out;
-// otherwise this is one piece of a split tile, and each row's output
-// normalized by its own sum goes to part_o (bf16, [256 rows][128]) with the
-// row's reference maximum (log2 domain) and sum to part_ml (rows
+// otherwise this is one piece of a split tile, and each row's unnormalized
+// output sums go to part_o (fp32, [256 rows][128]) with the row's integer
+// reference maximum (log2 domain) and weight sum to part_ml (rows
 // ml_row_stride pairs apart).  Every thread
 // of the kThreads-thread workgroup calls it; `smem` is the workgroup's LDS.
 template <int G>
 __device__ __forceinline__ void prefill_range(const PrefillArgs& a, int g, int r, int tile,
-                                              int kt_begin, int kt_end, uint16_t* part_o,
+                                              int kt_begin, int kt_end, float* part_o,
                                               float* part_ml, int ml_row_stride, PrefillLds& smem) {
   constexpr int TQ = kRowsWG / G;  // tokens per workgroup
   const int q0 = a.cu_seqlens[r];
@@ -275,8 +281,10 @@ __device__ __forceinline__ void prefill_range(const PrefillArgs& a, int g, int r
     mx = max_halves(mx) * qs;
     if (__ballot(mx > mref + kLazyRescale) != 0) {
       asm volatile("" ::: "memory");  // keep the rare rescale a real branch
-      const float mnew = fmaxf(mref, mx);
-      const float corr = fast_exp2(mref - mnew);
+      // integer references: the correction 2^(mref - mnew) is exact (0 for
+      // the first tile, where mref is still the -1e30 start value)
+      const float mnew = fmaxf(mref, ceilf(mx));
+      const float corr = ldexpf(1.0f, (int)fmaxf(mref - mnew, -200.0f));
       mref = mnew;
       lrun *= corr;
 #pragma unroll
@@ -355,15 +363,22 @@ __device__ __forceinline__ void prefill_range(const PrefillArgs& a, int g, int r
 
   const float ltot = sum_halves(lrun);
   if (!row_valid) return;
-  const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
-  uint16_t* orow;
   if (part_o) {
-    // one piece of a split tile: this row's normalized output and (m, l)
-    orow = part_o + rho * kHeadDim;
+    // one piece of a split tile: this row's unnormalized sums and (m, l)
+    float* prow = part_o + rho * kHeadDim;
     if (hf == 0) *reinterpret_cast<float2*>(part_ml + 2 * rho * ml_row_stride) = make_float2(mref, ltot);
-  } else {
-    orow = static_cast<uint16_t*>(a.out) + ((int64_t)(q0 + t0 + tok) * Hq + g * G + hh) * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * db + 8 * q4 + 4 * hf;
+        *reinterpret_cast<float4*>(prow + d0) =
+            make_float4(oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2], oacc[db][4 * q4 + 3]);
+      }
+    return;
   }
+  const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+  uint16_t* orow = static_cast<uint16_t*>(a.out) + ((int64_t)(q0 + t0 + tok) * Hq + g * G + hh) * kHeadDim;
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
 #pragma unroll

@@ -157,8 +157,9 @@ struct PrefillSplit {
   int32_t* header;          // [0] pieces planned, [1] split tiles
   int32_t* items;           // [max_items][8]: r, tile, kt_begin, kt_end, piece, pieces, split slot, 0
   int32_t* splits;          // [max_entries][4]: r, tile, pieces, 0
-  uint16_t* part_o;         // [max_entries][max_pieces][Hkv][256 rows][128] bf16, normalized
-  float* part_ml;           // [max_entries][Hkv][256 rows][max_pieces][2]: reference max (log2), sum
+  float* part_o;            // [max_entries][max_pieces][Hkv][256 rows][128] fp32, unnormalized
+  float* part_ml;           // [max_entries][Hkv][256 rows][max_pieces][2]: integer reference
+                            // max (log2 domain), weight sum
 };
 
 constexpr int kMaxPieceTiles = 1023;   // planner bins: piece lengths 1 .. 1023 tiles

@@ -40,7 +40,15 @@ def test_forced_split_ragged(qil, hq, hkv, kps):
     print("  max abs err split", np.max(np.abs(split - ref)), "unsplit", np.max(np.abs(whole - ref)),
           flush=True)
     assert H.excess(split, ref, "bf16") <= 0
-    assert np.max(np.abs(split - whole)) < 2e-2
+    # pieces keep fp32 sums over integer reference maxima, so the merge is
+    # the whole tile's O / l up to the order of fp32 additions: the two bf16
+    # outputs differ by at most one bf16 step (<= 2^-7 of the value) plus
+    # that reordering error (~1e-6 here; 1e-5 allowed)
+    diff = np.abs(split - whole)
+    bound = np.maximum(np.abs(split), np.abs(whole)) * 2.0 ** -7 + 1e-5
+    print(f"  split vs whole: {np.mean(split != whole):.2e} of the elements differ, "
+          f"max |diff| {diff.max():.3e}, max |diff|/bound {np.max(diff / bound):.3f}", flush=True)
+    assert np.all(diff <= bound)
 
 
 @pytest.mark.parametrize("page", [16, 256])
