@@ -251,6 +251,26 @@ int qil_paged_decode(void* out, const void* q, const void* k_cache, const void* 
                      void* stream);
 
 /*
+ * qil_paged_decode_no_alloc -- qil_paged_decode for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments and
+ * results as qil_paged_decode without workspace / workspace_bytes: the split
+ * partials and the request order go to a fixed scratch array inside the
+ * library, 32 MiB per GPU, held from the first call on that GPU until the
+ * process ends.  A call that would need more (qil_paged_decode_workspace_size
+ * above 33,554,432 bytes) returns QIL_EWORKSPACE before anything is enqueued.
+ * The call allocates nothing.  All calls on one GPU share its array and its
+ * contents need not start at zero: calls that overlap on one GPU (several
+ * streams or threads at once) race; calls in order on one stream do not.
+ */
+int qil_paged_decode_no_alloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, int32_t block_table_stride,
+                              const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                              int32_t num_pages, int32_t max_context_len, float scale,
+                              int32_t dtype, int32_t keys_per_split, void* stream);
+
+/*
  * qil_paged_decode_append -- the decode step's write and decode in one call:
  * the same result as qil_kv_write(k_new, v_new, slot_mapping) followed by
  * qil_paged_decode(...), for a batch whose new token of request r sits at

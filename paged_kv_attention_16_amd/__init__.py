@@ -10,6 +10,7 @@ The functions mirror the C ABI in include/qil.h:
   kv_write(k, v, k_cache, v_cache, slot_mapping, page_size=..., fuse=None)
   rope_cos_sin(table, theta)
   paged_decode(out, q, k_cache, v_cache, block_tables, context_lens, ...)
+  paged_decode_no_alloc(out, q, k_cache, v_cache, block_tables, context_lens, ...)
   paged_decode_append(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, ...)
   paged_prefill(out, q, k_cache, v_cache, block_tables, cu_seqlens_q, context_lens, ...)
   paged_attention_mixed(k_cache, v_cache, scale, decode=..., prefill=...)
@@ -22,7 +23,8 @@ import os
 
 __all__ = [
     "QilError", "lib_path", "load", "version", "kv_write", "QKNormRope", "rope_cos_sin",
-    "paged_decode", "paged_decode_workspace_size", "paged_decode_append", "paged_prefill",
+    "paged_decode", "paged_decode_workspace_size", "paged_decode_no_alloc", "paged_decode_append",
+    "paged_prefill",
     "paged_prefill_workspace_size",
     "paged_attention_mixed",
     "qkv_proj_write", "qkv_proj_workspace_size", "set_debug", "debug_enabled",
@@ -110,6 +112,9 @@ def load(path=None):
     lib.qil_paged_decode.restype = ctypes.c_int
     lib.qil_paged_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
                                      i32, f32, i32, i32, vp, sz, vp]
+    lib.qil_paged_decode_no_alloc.restype = ctypes.c_int
+    lib.qil_paged_decode_no_alloc.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
+                                              i32, i32, f32, i32, i32, vp]
     lib.qil_paged_decode_append.restype = ctypes.c_int
     lib.qil_paged_decode_append.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int64, vp, vp,
                                             vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32,
@@ -381,6 +386,24 @@ def paged_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_conte
         int(block_tables.shape[1]), _ptr(context_lens), batch, hq, hkv, d, page, num_pages,
         int(max_context_len), float(scale), _dtype_code(q), int(keys_per_split),
         _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc)
+
+
+def paged_decode_no_alloc(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                          scale, keys_per_split=0, stream=None):
+    """paged_decode with the library's fixed 32 MiB scratch array as its
+    workspace: nothing is allocated (for graph capture and callers that may
+    not allocate); calls that overlap on one GPU race."""
+    num_pages, hkv, page, d = _pools(k_cache, v_cache)
+    _rows(q, out, "q", "out", k_cache)
+    batch, hq = int(q.shape[0]), int(q.shape[1])
+    _i32(block_tables, "block_tables", k_cache, batch, dims=2)
+    _i32(context_lens, "context_lens", k_cache, batch)
+    _on_gpu(k_cache)
+    rc = load().qil_paged_decode_no_alloc(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(context_lens), batch, hq, hkv, d, page, num_pages,
+        int(max_context_len), float(scale), _dtype_code(q), int(keys_per_split), _stream(stream))
     _check(rc)
 
 

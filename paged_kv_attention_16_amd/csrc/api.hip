@@ -12,6 +12,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include <hip/hip_runtime.h>
 
@@ -238,6 +239,36 @@ hipError_t check_prefill_metadata(const qil::PrefillArgs& a, qil::DebugReport* r
     e = qil::launch_check_tables(a.block_tables, a.bt_stride, a.context_lens, a.batch, a.log2_page,
                                  a.num_pages, a.max_context_len, rep, s);
   return e;
+}
+
+// ---- fixed scratch of qil_paged_decode_no_alloc ----------------------------
+// The decode workspace (split partials and the request order) for callers
+// that cannot allocate: one array per GPU, held until the process ends.  In
+// host code `scratch` names a host-side stand-in; kernels get the device
+// address resolved once per device by hipGetSymbolAddress.  Every call on one
+// GPU shares the array, and nothing in it has to start at zero (the decode
+// kernels write every entry they later read), so calls that overlap on one
+// GPU race.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+hipError_t device_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 // Validate a decode call and fill its launch arguments.  *empty is set when
@@ -677,6 +708,44 @@ int qil_paged_decode(void* out, const void* q, const void* k_cache, const void* 
     if (rc) return rc;
   }
   hipError_t e = qil::launch_decode(a, s);
+  if (e != hipSuccess) return fail(QIL_EHIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int qil_paged_decode_no_alloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, int32_t block_table_stride,
+                              const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                              int32_t num_pages, int32_t max_context_len, float scale,
+                              int32_t dtype, int32_t keys_per_split, void* stream) {
+  // Every check first, on the host: the arguments (with a stand-in workspace
+  // of the scratch array's size), then the scratch the call needs.
+  qil::DecodeArgs a;
+  bool empty = false;
+  int rc = prep_decode(out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens,
+                       batch, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                       max_context_len, scale, dtype, keys_per_split,
+                       reinterpret_cast<void*>(kScratchBytes), kScratchBytes, a, &empty);
+  if (rc == QIL_EWORKSPACE) {
+    const SplitPlan p = plan_splits(batch, num_kv_heads, max_context_len, keys_per_split);
+    return fail(QIL_EWORKSPACE, "this decode needs %zu bytes of scratch; the library's fixed scratch "
+                "array holds %zu", workspace_bytes_for(batch, num_q_heads, num_kv_heads, p),
+                kScratchBytes);
+  }
+  if (rc || empty) return rc;
+  void* scratch_ptr = nullptr;
+  hipError_t e = device_scratch(&scratch_ptr);
+  if (e != hipSuccess) return fail(QIL_EHIP, "scratch address: %s", hipGetErrorString(e));
+  rc = prep_decode(out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens, batch,
+                   num_q_heads, num_kv_heads, head_dim, page_size, num_pages, max_context_len,
+                   scale, dtype, keys_per_split, scratch_ptr, kScratchBytes, a, &empty);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_on()) {
+    rc = run_checks(s, [&](qil::DebugReport* rep) { return check_decode_metadata(a, rep, s); });
+    if (rc) return rc;
+  }
+  e = qil::launch_decode(a, s);
   if (e != hipSuccess) return fail(QIL_EHIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -256,3 +256,21 @@ def test_debug_switch(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(qil.QilError):
         qil.load(str(tmp_path / "missing.so"))
+
+
+def test_decode_no_alloc_rejects_above_its_scratch(lib):
+    """The fixed-scratch decode refuses, before any HIP call, a shape whose
+    workspace would exceed the library's 32 MiB array."""
+    def call(**kw):
+        a = dict(B=2, hq=16, hkv=8, maxL=2048, S=0, bts=128)
+        a.update(kw)
+        return lib.qil_paged_decode_no_alloc(FAKE, FAKE, FAKE, FAKE, FAKE, a["bts"], FAKE, a["B"],
+                                             a["hq"], a["hkv"], 128, 16, 8192, a["maxL"], 0.088, 1,
+                                             a["S"], None)
+    big = dict(B=4096, hq=64, hkv=8, maxL=16384, S=1024, bts=1024)
+    need = lib.qil_paged_decode_workspace_size(4096, 64, 8, 16384, 16, 1024)
+    assert need > 32 << 20
+    assert call(**big) == EWS
+    assert b"scratch" in lib.qil_last_error()
+    assert call(hq=12) == EINVAL                    # the usual checks run too
+    assert call(S=100) == EINVAL
