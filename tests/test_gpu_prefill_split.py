@@ -12,6 +12,7 @@ import torch
 
 import paged_kv_attention_16_amd as qil
 from tests import harness as H
+from oracle.bf16 import bf16_to_f64
 from workloads import bf16_from_f32, make_custom, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -40,14 +41,23 @@ def test_forced_split_ragged(qil, hq, hkv, kps):
     print("  max abs err split", np.max(np.abs(split - ref)), "unsplit", np.max(np.abs(whole - ref)),
           flush=True)
     assert H.excess(split, ref, "bf16") <= 0
-    # pieces keep fp32 sums over integer reference maxima, so the merge is
-    # the whole tile's O / l up to the order of fp32 additions: the two bf16
-    # outputs differ by at most one bf16 step (<= 2^-7 of the value) plus
-    # that reordering error (~1e-6 here; 1e-5 allowed)
+    # Pieces keep fp32 sums over integer reference maxima, so the merge adds
+    # no rounding of its own.  What still differs is the reference each
+    # weight is formed against: exp2 of (score - reference) in fp32 can land
+    # on the other side of a bf16 rounding boundary (probability ~2^-15 per
+    # weight), and one weight moving by one bf16 step (2^-8 of itself) moves
+    # the output by at most 2^-8 |v - o|.  Bar: at least 99.9 % of the
+    # elements identical, and each within one output step plus that one-flip
+    # term (|v| <= max |v| of the inputs) plus 1e-5 for fp32 addition order.
     diff = np.abs(split - whole)
-    bound = np.maximum(np.abs(split), np.abs(whole)) * 2.0 ** -7 + 1e-5
-    print(f"  split vs whole: {np.mean(split != whole):.2e} of the elements differ, "
-          f"max |diff| {diff.max():.3e}, max |diff|/bound {np.max(diff / bound):.3f}", flush=True)
+    vmax = float(np.max(np.abs(bf16_to_f64(np.concatenate([case.data["v_cached"],
+                                                            case.data["v_new"]])))))
+    mag = np.maximum(np.abs(split), np.abs(whole))
+    bound = mag * 2.0 ** -7 + 2.0 ** -8 * (vmax + mag) + 1e-5
+    same = np.mean(split == whole)
+    print(f"  split vs whole: {1 - same:.2e} of the elements differ, max |diff| {diff.max():.3e}, "
+          f"max |diff|/bound {np.max(diff / bound):.3f}", flush=True)
+    assert same >= 0.999
     assert np.all(diff <= bound)
 
 
