@@ -76,6 +76,21 @@ __device__ __forceinline__ int acc_row(int v, int hf) { return 8 * (v >> 2) + 4 
 __device__ __forceinline__ int k_chunk(int row, int c) { return c ^ (row & 15); }
 __device__ __forceinline__ int v_chunk(int row, int c) { return c ^ ((row & 3) << 2); }
 
+// One 16-byte LDS-DMA load per lane (global_load_lds_dwordx4): lane l's
+// bytes land at dst + 16 l.  Written as assembly so that the compiler does not
+// track it.  With the builtin, the compiler cannot tell which of the two tile
+// buffers a load writes, so before the current tile's first transposing read
+// it waited for every load in flight, the next tile's included, and part of
+// that tile's load latency sat inside the current tile (measured: 4-6 %
+// on prefill-varlen and the 8B step's prefill).  The tile loop waits for its
+// own loads (vmcnt 0 before each workgroup barrier).  The s_nop covers the
+// wait state that a write of M0 needs before an LDS-DMA instruction.  No
+// register is written.
+__device__ __forceinline__ void lds_dma16(const char* src, lds_char* dst) {
+  const unsigned m0 = (unsigned)(uintptr_t)dst;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
+}
+
 // Maximum / sum over the two halves of a wavefront (lanes l and l ^ 32),
 // with v_permlane32_swap instead of an LDS round trip.
 __device__ __forceinline__ float max_halves(float x) {
@@ -190,8 +205,8 @@ __device__ __forceinline__ void prefill_range(const PrefillArgs& a, int g, int r
       lds_char* kdst = (lds_char*)&smem[buf][0][0] + (kRowsPerWave * w + 4 * m2) * 256;
       lds_char* vdst = (lds_char*)&smem[buf][1][0] + (kRowsPerWave * w + 4 * m2) * 256;
       if (key < L) {
-        __builtin_amdgcn_global_load_lds(kpool + grow * 256 + 16 * k_chunk(row, lpc), kdst, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vpool + grow * 256 + 16 * v_chunk(row, lpc), vdst, 16, 0, 0);
+        lds_dma16(kpool + grow * 256 + 16 * k_chunk(row, lpc), kdst);
+        lds_dma16(vpool + grow * 256 + 16 * v_chunk(row, lpc), vdst);
       }
     }
   };
