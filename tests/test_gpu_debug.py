@@ -96,6 +96,29 @@ def test_decode_tables(debug):
                   "context_lens[0]")
 
 
+def test_decode_append_context_past_table(debug):
+    """A context past the host bound is reported by the debug checks of the
+    fused decode step, and the slot check reads no block-table entry past the
+    request's row (it stops at min(max_context_len, stride * page_size))."""
+    qil = debug
+    w = make_custom([40, 300, 17], [1, 1, 1], page=16, seed=83, decode=True)
+    c = H.DeviceCase(w, DEV, write_new=False)
+    q = c.q_all.contiguous()
+    out = torch.empty_like(q)
+    stride = int(c.bt.shape[1])
+    maxl = stride * w.page_size                 # the largest host bound the table allows
+    ctx = c.ctx.clone()
+    ctx[0] = maxl + 1                           # row 0: one key past its block-table row
+    expect_einval(lambda: qil.paged_decode_append(out, q, c.k_new, c.v_new, c.new_slots, c.kp, c.vp,
+                                                  c.bt, ctx, maxl, float(w.scale)),
+                  "context_lens[0]")
+    # valid metadata still runs under the checks
+    qil.paged_decode_append(out, q, c.k_new, c.v_new, c.new_slots, c.kp, c.vp, c.bt, c.ctx, maxl,
+                            float(w.scale))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+
+
 def test_prefill_cu_seqlens(debug):
     qil = debug
     w, c = small_case()
