@@ -1059,9 +1059,9 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "qil_paged_decode (the decode call of the two-call step): decode_order_kernel "
-                      "(longest requests first) then decode_mfma_kernel<2>, one split per request, "
-                      "no merge pass; the launch time covers both",
+            "kernel": "qil_paged_decode (the decode call of the two-call step): one launch of "
+                      "decode_mfma_kernel<2>, one split per request, each workgroup ranking the "
+                      "batch longest first itself; no ordering or merge launch",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -323,6 +323,8 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a) {
 // LDS atomics; the order inside a bucket does not matter, since every
 // request's result is independent of which workgroup computes it) and
 // writes the permutation that the decode grid reads its request ids through.
+// The bf16 kernel ranks batches of up to 256 requests itself
+// (decode_rank_request) and skips this launch.
 constexpr int kOrderBuckets = 256;
 constexpr int kOrderThreads = 1024;
 
@@ -384,14 +386,24 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(const int32
 
 template <int G, bool BF16>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
-  hipError_t e = launch_decode_order(a, s);
-  if (e != hipSuccess) return e;
   dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
-  if constexpr (BF16)
-    hipLaunchKernelGGL((decode_mfma_kernel<G>), grid, dim3(64 * kMW), 0, s, a);
-  else
+  if constexpr (BF16) {
+    if (a.order != nullptr && a.batch <= kRankMaxBatch) {
+      // the workgroups rank the batch themselves: no ordering launch
+      DecodeArgs ai = a;
+      ai.rank_inline = true;
+      hipLaunchKernelGGL((decode_mfma_kernel<G>), grid, dim3(64 * kMW), 0, s, ai);
+    } else {
+      hipError_t e = launch_decode_order(a, s);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((decode_mfma_kernel<G>), grid, dim3(64 * kMW), 0, s, a);
+    }
+  } else {
+    hipError_t e = launch_decode_order(a, s);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_f32_kernel<G>), grid, dim3(64 * kFW), 0, s, a);
-  e = hipGetLastError();
+  }
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_splits == 1) return e;
   hipLaunchKernelGGL((decode_merge_kernel<BF16>), dim3(a.num_q_heads, a.batch), dim3(128), 0, s, a);
   return hipGetLastError();

@@ -326,10 +326,91 @@ __device__ __forceinline__ void decode_mfma_split(const DecodeArgs& a, int split
   }
 }
 
+// Longest-first order inside the workgroup, for batches of at most
+// kRankMaxBatch requests: every workgroup (of 64 W >= 256 threads) sorts the
+// batch the same way and keeps the request at its own grid row z.  The sort
+// is a stable counting sort over 256 buckets of decreasing context length
+// (bucket 0 holds the longest), ties in request order, so every workgroup
+// derives the same permutation: the bucket that holds position z comes from
+// the histogram's prefix sum, and the request inside it from one ballot per
+// wavefront over the bucket's members.  Threads 0..255 hold one request and
+// one bucket each.  No global writes; it replaces a separate ordering launch
+// and the dependent read of its result.  Larger batches measured slower this
+// way (each workgroup reads every length) and keep the ordering launch.
+constexpr int kRankMaxBatch = 256;
+
+template <int W>
+__device__ __forceinline__ int decode_rank_request(const int32_t* context_lens, int batch,
+                                                   int max_len, int z) {
+  static_assert(64 * W >= kRankMaxBatch, "a thread per bucket and per request");
+  constexpr int kRankWaves = kRankMaxBatch / 64;
+  __shared__ int hist[kRankMaxBatch];
+  __shared__ int wave_sum[kRankWaves];
+  __shared__ unsigned long long members[kRankWaves];
+  __shared__ int pick[3];  // bucket of position z, its offset in the bucket, the request
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const bool holder = tid < kRankMaxBatch;  // whole wavefronts
+  if (holder) hist[tid] = 0;
+  if (tid == 0) {
+    pick[0] = -1;
+    pick[2] = z;  // stays in range even if no bucket claims z
+  }
+  int b = -1;  // bucket of request tid
+  if (tid < batch) {
+    int L = context_lens[tid];
+    L = L < 0 ? 0 : (L > max_len ? max_len : L);
+    b = (int)((int64_t)(max_len - L) * kRankMaxBatch / ((int64_t)max_len + 1));
+  }
+  __syncthreads();
+  if (b >= 0) atomicAdd(&hist[b], 1);
+  __syncthreads();
+  // exclusive prefix sum over the buckets, thread t holding bucket t
+  int own = 0, v = 0;
+  if (holder) {
+    own = v = hist[tid];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(v, o);
+      if (lane >= o) v += t;
+    }
+    if (lane == 63) wave_sum[wv] = v;
+  }
+  __syncthreads();
+  if (holder) {
+    int start = v - own;
+    for (int i = 0; i < wv; ++i) start += wave_sum[i];
+    if (z >= start && z < start + own) {
+      pick[0] = tid;
+      pick[1] = z - start;
+    }
+  }
+  __syncthreads();
+  const int pb = pick[0];
+  unsigned long long m = 0;
+  if (holder) {
+    m = __ballot(b == pb);
+    if (lane == 0) members[wv] = m;
+  }
+  __syncthreads();
+  if (b >= 0 && b == pb) {
+    // members before request tid: those of lower wavefronts and lower lanes
+    int rank = __popcll(m & ((1ull << lane) - 1));
+    for (int i = 0; i < wv; ++i) rank += __popcll(members[i]);
+    if (rank == pick[1]) pick[2] = tid;
+  }
+  __syncthreads();
+  return pick[2];
+}
+
 template <int G>
 __global__ __launch_bounds__(64 * kMW) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) DecodeRing smem[kMW];
-  const int r = a.order != nullptr ? a.order[blockIdx.z] : (int)blockIdx.z;
+  int r = blockIdx.z;
+  if (a.rank_inline)
+    r = decode_rank_request<kMW>(a.context_lens, a.batch, a.max_context_len, r);
+  else if (a.order != nullptr)
+    r = a.order[r];
   decode_mfma_split<G, kMW>(a, blockIdx.x, blockIdx.y, r, smem);
 }
 

@@ -13,8 +13,8 @@
 // go to the 8 XCDs round robin, so each prefill block keeps its KV head's
 // XCD (KV head = block index mod 8 when num_kv_heads = 8), as in the
 // prefill-only launch.  On large decode grids the decode blocks take their
-// requests longest first, through the order that qil_paged_decode's ordering
-// kernel writes.
+// requests longest first, in the order qil_paged_decode uses (ranked by each
+// block for batches up to 256, else written by the ordering kernel).
 #include "decode_body.h"
 #include "prefill_body.h"
 
@@ -54,8 +54,11 @@ __global__ __launch_bounds__(kThreads) void mixed_kernel(PrefillArgs pa, int n_q
     // requests longest first when the order pass ran
     const int split = idx % da.num_splits;
     const int rest = idx / da.num_splits;
-    const int zr = rest / da.num_kv_heads;
-    const int r = da.order != nullptr ? da.order[zr] : zr;
+    int r = rest / da.num_kv_heads;
+    if (da.rank_inline)
+      r = decode_rank_request<kMixedWaves>(da.context_lens, da.batch, da.max_context_len, r);
+    else if (da.order != nullptr)
+      r = da.order[r];
     decode_mfma_split<G, kMixedWaves>(da, split, rest % da.num_kv_heads, r,
                                       reinterpret_cast<DecodeRing*>(lds));
   }
@@ -70,12 +73,17 @@ hipError_t launch_g(const PrefillArgs& pa, const DecodeArgs& da, hipStream_t s) 
   const int64_t blocks = 8 * ((n_pre + 7) / 8 + (n_dec + 7) / 8);
   if (blocks == 0) return hipSuccess;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  DecodeArgs di = da;
   if (n_dec > 0) {
-    hipError_t e = launch_decode_order(da, s);
-    if (e != hipSuccess) return e;
+    if (da.order != nullptr && da.batch <= kRankMaxBatch) {
+      di.rank_inline = true;  // the decode blocks rank the batch themselves
+    } else {
+      hipError_t e = launch_decode_order(da, s);
+      if (e != hipSuccess) return e;
+    }
   }
   hipLaunchKernelGGL((mixed_kernel<G>), dim3((unsigned)blocks), dim3(kThreads), 0, s, pa, n_qtiles,
-                     (int)n_pre, da, (int)n_dec);
+                     (int)n_pre, di, (int)n_dec);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || da.batch == 0 || da.num_splits == 1) return e;
   return launch_decode_merge(da, s);

@@ -96,6 +96,8 @@ struct DecodeArgs {
   float* ws_l;             // [batch][Hq][num_splits]
   int32_t* order;          // [batch] requests by decreasing context length, or null
                            // (then request r is grid row r)
+  bool rank_inline;        // the bf16 decode workgroups derive the longest-first
+                           // order themselves (set by the launcher, batch <= 256)
   bool bf16;
   // Append (bf16 matrix-core kernel only; null = plain decode): request r's
   // new token at position context_lens[r] - 1 has K/V rows k_new/v_new

@@ -69,12 +69,17 @@ def test_longest_first_order_is_invisible(qil, split):
     print(f"split {split}: {len(groups)} groups of 4 match the full batch bit for bit", flush=True)
 
 
-@pytest.mark.parametrize("dtype,batch,page", [("bf16", 3000, 16), ("f32", 200, 32)])
+@pytest.mark.parametrize("dtype,batch,page", [("bf16", 3000, 16), ("bf16", 256, 16),
+                                               ("bf16", 257, 16), ("f32", 200, 32)])
 def test_ordered_large_batches(qil, dtype, batch, page):
     """Grids far past one round of the GPU run longest first: 3,000 bf16
-    requests (the ordering kernel's strided loops) and 200 fp32 requests,
-    contexts from 1 to a few hundred keys.  Sampled requests against the
-    oracle, and bit equality with the same requests decoded 3 at a time."""
+    requests (the ordering kernel's strided loops), 256 bf16 requests (the
+    most that the decode workgroups rank themselves) and 257 (the first batch
+    that takes the ordering kernel), and 200 fp32 requests, contexts from 1 to
+    a few hundred keys (many equal lengths).
+    Every output row is written (the output starts as NaN), sampled requests
+    match the oracle, and the same requests decoded 3 at a time match bit for
+    bit."""
     rng = np.random.default_rng(batch)
     ctx = rng.integers(1, 400 if dtype == "bf16" else 300, size=batch)
     w = make_custom(ctx, np.ones(batch, np.int64), page=page, dtype=dtype, seed=batch % 97,
@@ -85,7 +90,10 @@ def test_ordered_large_batches(qil, dtype, batch, page):
                         rng.choice(batch, 10, replace=False).tolist()))
     got, ref = H.run_decode_case(w, DEV, requests=sample, keys_per_split=256, case=case)
     assert H.excess(got, ref, dtype) <= 0
-    full = H.to_bits(case.decode(keys_per_split=256))
+    out = torch.full_like(case.q_all, float("nan"))
+    full_out = case.decode(keys_per_split=256, out=out)
+    assert bool(torch.isfinite(full_out).all()), "a request of the batch was not decoded"
+    full = H.to_bits(full_out)
     for i in range(0, len(sample), 3):
         grp = sample[i:i + 3]
         assert np.array_equal(full[grp], H.to_bits(case.decode(requests=grp, keys_per_split=256)))
