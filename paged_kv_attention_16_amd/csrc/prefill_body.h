@@ -148,6 +148,12 @@ __device__ __forceinline__ void prefill_range(const PrefillArgs& a, int g, int r
   const int hh = rho % G;
   const bool row_valid = tok < tvalid;
   const int my_pos = prefix + t0 + min(tok, tvalid - 1);
+  // Keys this wavefront's rows see: up to its last valid token's position.
+  // A wavefront whose rows all lie past the tile's tokens (the last query
+  // tile of a request) has none.
+  const int wtok_lo = (32 * w) / G, wtok_hi = (32 * w + 31) / G;
+  const bool wave_rows = wtok_lo < tvalid;
+  const int wpos_max = prefix + t0 + min(wtok_hi, tvalid - 1);
 
   // Loader role.  Wavefront w fills rows 8w .. 8w+7 of the K and V tiles,
   // 4 rows (1 KB) per instruction: lane l lands at byte 16 l of that KB,
@@ -327,9 +333,15 @@ __device__ __forceinline__ void prefill_range(const PrefillArgs& a, int g, int r
     }
   };
 
-  // One tile as two 32-key halves.
+  // One tile as two 32-key halves.  A wavefront without valid rows skips
+  // every tile, and on the diagonal one skips the tiles that lie wholly past
+  // its last row's position: their weights would all be exactly 0.  It still
+  // loads its share of every tile and meets every barrier; the gain is the
+  // LDS operand reads it leaves to the other wavefronts of the CU.
   auto compute = [&](auto mask_tag, int buf, int kt) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int kbase = kt * kBN;
+    if (!wave_rows || (MASK && kbase > wpos_max)) return;  // uniform per wavefront
     bf16x8_t kop[8];
     bf16x8_t vop[4][2];
     bf16x8_t p0[2], p1[2];
