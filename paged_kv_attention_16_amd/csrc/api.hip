@@ -345,9 +345,10 @@ int prep_decode(void* out, const void* q, const void* k_cache, const void* v_cac
   return QIL_OK;
 }
 
-// Split plan of a prefill call (host integers only).  The grid of whole
-// query tiles has one workgroup per CU at a time (8 waves of 205 registers);
-// when it holds at most 128 tiles with rows, one round of long tiles sets
+// Split plan of a prefill call (host integers only), counted in query tiles
+// of 256 rows (8 waves, one workgroup per CU at a time; an unsplit call over
+// short contexts runs its whole tiles as 128-row workgroups, two per CU).
+// When the grid holds at most 128 tiles with rows, one round of long tiles sets
 // the time while half the CUs or more idle.  Such calls cut every query tile
 // into n = 256 / tiles pieces (rounded down: all pieces still fit one round),
 // that is at most S = ceil(kt_max / n) 64-key tiles each, and at least 16.

@@ -12,7 +12,9 @@
 // request and one KV head: 256/G consecutive new tokens times the G query
 // heads that share the KV head (GQA packing), so each K/V tile fetched from
 // HBM/L2 serves 256 rows.  Each wavefront owns 32 rows.  The workgroup walks
-// key tiles of 64 keys up to its last visible key.
+// key tiles of 64 keys up to its last visible key.  Whole query tiles over
+// short contexts run as workgroups of 4 wavefronts (128 rows), two per CU;
+// each row's arithmetic is the same in either shape.
 //
 //   * Tiles go from memory straight into LDS (global_load_lds, 16 bytes per
 //     lane, no staging registers): K and V rows land row-major with the
@@ -102,10 +104,13 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
+// The split-over-keys path and the one-launch mixed step use workgroups of
+// 8 wavefronts (256 query rows).  Whole query tiles also run as workgroups
+// of 4 wavefronts (128 rows, two workgroups per CU) when the keys per tile
+// are few (see launch_prefill).
 constexpr int kWaves = 8;               // wavefronts per workgroup, 32 query rows each
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsWG = 32 * kWaves;    // query rows per workgroup
-constexpr int kRowsPerWave = kBN / kWaves;  // tile rows each wavefront loads
 
 // LDS of one workgroup: [slot][K | V][64 rows x 256 bytes].
 typedef char PrefillLds[2][2][kBN * 256];
@@ -115,13 +120,16 @@ typedef char PrefillLds[2][2][kBN * 256];
 // otherwise this is one piece of a split tile, and each row's unnormalized
 // output sums go to part_o (fp32, [256 rows][128]) with the row's integer
 // reference maximum (log2 domain) and weight sum to part_ml (rows
-// ml_row_stride pairs apart).  Every thread
-// of the kThreads-thread workgroup calls it; `smem` is the workgroup's LDS.
-template <int G>
+// ml_row_stride pairs apart).  Every thread of the workgroup of W
+// wavefronts (32 W query rows) calls it; `smem` is the workgroup's LDS.
+template <int G, int W = kWaves>
 __device__ __forceinline__ void prefill_range(const PrefillArgs& a, int g, int r, int tile,
                                               int kt_begin, int kt_end, float* part_o,
                                               float* part_ml, int ml_row_stride, PrefillLds& smem) {
-  constexpr int TQ = kRowsWG / G;  // tokens per workgroup
+  static_assert(W == 4 || W == 8, "4 or 8 wavefronts");
+  constexpr int kWGThreads = 64 * W;
+  constexpr int kRowsPerWave = kBN / W;  // tile rows each wavefront loads
+  constexpr int TQ = 32 * W / G;         // tokens per workgroup
   const int q0 = a.cu_seqlens[r];
   // rows of this request, kept inside [0, total_q)
   const int n = min(a.cu_seqlens[r + 1], a.total_q) - max(q0, 0);
@@ -197,7 +205,7 @@ __device__ __forceinline__ void prefill_range(const PrefillArgs& a, int g, int r
   // to be finite: start from zeros.
   {
     uint4* zf = reinterpret_cast<uint4*>(&smem[0][0][0]);
-    for (int i = tid; i < (int)(sizeof(PrefillLds) / 16); i += kThreads) zf[i] = make_uint4(0, 0, 0, 0);
+    for (int i = tid; i < (int)(sizeof(PrefillLds) / 16); i += kWGThreads) zf[i] = make_uint4(0, 0, 0, 0);
   }
 
   auto issue_tile = [&](int kt, int buf) __attribute__((always_inline)) {
@@ -421,16 +429,18 @@ __device__ __forceinline__ void prefill_range(const PrefillArgs& a, int g, int r
 
 // One whole query tile, z counted from the last tile (z = 0 is the tile with
 // the most keys).
-template <int G>
+template <int G, int W = kWaves>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int n_qtiles, int g, int r,
                                              int z, PrefillLds& smem) {
-  prefill_range<G>(a, g, r, n_qtiles - 1 - z, 0, 1 << 30, nullptr, nullptr, 0, smem);
+  prefill_range<G, W>(a, g, r, n_qtiles - 1 - z, 0, 1 << 30, nullptr, nullptr, 0, smem);
 }
 
-template <int G>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int n_qtiles) {
+// W = 8: one workgroup per CU; W = 4: two per CU (two wavefronts per SIMD
+// either way, at most 256 registers each).
+template <int G, int W>
+__global__ __launch_bounds__(64 * W, 2) void prefill_kernel(PrefillArgs a, int n_qtiles) {
   __shared__ __attribute__((aligned(1024))) PrefillLds smem;
-  prefill_tile<G>(a, n_qtiles, blockIdx.x, blockIdx.y, blockIdx.z, smem);
+  prefill_tile<G, W>(a, n_qtiles, blockIdx.x, blockIdx.y, blockIdx.z, smem);
 }
 
 }  // namespace

@@ -99,6 +99,26 @@ def test_ordered_large_batches(qil, dtype, batch, page):
         assert np.array_equal(full[grp], H.to_bits(case.decode(requests=grp, keys_per_split=256)))
 
 
+def test_ranked_small_batch_many_splits(qil):
+    """A batch of 3 whose grid still takes the longest-first order (3 requests
+    x 8 KV heads x 24 splits of 256 keys = 576 workgroups), so every
+    workgroup ranks the 3 requests itself, two of them with nearly equal
+    lengths.  All rows are written, match the oracle, and match each request
+    decoded alone (a 192-workgroup grid in batch order) bit for bit."""
+    ctx = [6000, 100, 6001]
+    w = make_custom(ctx, [1, 1, 1], page=16, seed=31, decode=True)
+    case = H.DeviceCase(w, DEV)
+    out = torch.full_like(case.q_all, float("nan"))
+    full_out = case.decode(keys_per_split=256, out=out)
+    assert bool(torch.isfinite(full_out).all())
+    torch.cuda.synchronize()
+    ref = H.OracleCase(w, case.data, range(3)).attention(range(3))
+    assert H.excess(H.to_f64(full_out), ref, "bf16") <= 0
+    full = H.to_bits(full_out)
+    for r in range(3):
+        assert np.array_equal(full[[r]], H.to_bits(case.decode(requests=[r], keys_per_split=256)))
+
+
 def test_run_twice_bitwise(qil):
     w = make_workload(2)
     case = H.DeviceCase(w, DEV)

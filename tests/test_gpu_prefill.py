@@ -32,6 +32,35 @@ def test_group_sizes_ragged(qil, hq, hkv):
     assert H.excess(got, ref, "bf16") <= 0
 
 
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (32, 8), (40, 8), (64, 4)])
+def test_loose_context_bound_is_invisible(qil, hq, hkv):
+    """max_context_len is a host bound on the contexts; any value at least the
+    longest context gives the same output bit for bit.  A bound of 4,096 keys
+    (block tables padded with -1 columns to fit it) also switches the whole-
+    tile kernel from workgroups of 128 query rows (two per CU) to 256, so both
+    shapes run on the same inputs, and both match the oracle."""
+    ctx = [1, 65, 200, 129, 700, 33, 2000]
+    new = [1, 1, 200, 64, 131, 17, 1500]
+    w = make_custom(ctx, new, hq=hq, hkv=hkv, page=16, seed=hq + hkv)
+    case = H.DeviceCase(w, DEV)
+    tight = case.prefill()
+    reqs = np.asarray(w.prefill_idx)
+    rows = torch.from_numpy(case.rows_of(reqs)).to(DEV)
+    q = case.q_all.index_select(0, rows).contiguous()
+    bt = case.bt.index_select(0, torch.from_numpy(reqs).to(DEV))
+    pad = torch.full((bt.shape[0], 4096 // 16 - bt.shape[1]), -1, dtype=bt.dtype, device=DEV)
+    bt = torch.cat([bt, pad], dim=1).contiguous()
+    ctx_d = case.ctx.index_select(0, torch.from_numpy(reqs).to(DEV)).contiguous()
+    cu = H.i32(w.cu_seqlens(reqs), DEV)
+    loose = torch.empty_like(q)
+    qil.paged_prefill(loose, q, case.kp, case.vp, bt, cu, ctx_d, int(w.new_lens.max()), 4096,
+                      float(w.scale))
+    torch.cuda.synchronize()
+    assert torch.equal(tight.view(torch.int16), loose.view(torch.int16))
+    ref = H.OracleCase(w, case.data, range(w.batch)).attention(range(w.batch))
+    assert H.excess(H.to_f64(loose), ref, "bf16") <= 0
+
+
 @pytest.mark.parametrize("page", [32, 64, 256])
 def test_page_sizes(qil, page):
     got, ref = H.run_small_prefill(DEV, [300, 1000, 90], [100, 257, 90], 16, 8, page, seed=page)
