@@ -921,7 +921,7 @@ def sources_sha256(files):
 # grid is the bench's one-off pool fill.
 TRAFFIC_KERNELS = {
     "decode-b256": ("decode_mfma_kernel<2>", "largest"),
-    "prefill-varlen": ("prefill_kernel<2>", "largest"),
+    "prefill-varlen": ("prefill_kernel<2, 4>", "largest"),   # 128-row workgroups (short contexts)
     "qkv-proj-8b": ("qkv_proj_kernel<4, false>", "largest"),
     "kv-write-chunk": ("kv_write_kernel<16>", "frequent"),     # the 8,946-token chunk write
     "fused-write-8b": ("kv_write_fused_kernel", "frequent"),   # 2,112 tokens of qkv-proj-8b
