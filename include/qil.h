@@ -232,10 +232,12 @@ int qil_qkv_proj_write(const void* x, int64_t x_token_stride, const void* weight
  *                  that size is 0); its contents on entry do not matter.  It
  *                  holds the split partials when a request spans several
  *                  splits, and, when the grid has at least 512 workgroups
- *                  (batch * num_kv_heads * splits), the order in which the
- *                  requests are run: a first small kernel sorts them by
- *                  decreasing context length so that the longest start first.
- *                  Results do not depend on that order.
+ *                  (batch * num_kv_heads * splits), room for the order in
+ *                  which the requests are run, longest context first: bf16
+ *                  batches of up to 256 requests are ranked by the decode
+ *                  workgroups themselves, larger ones and fp32 by a first
+ *                  small kernel that writes the order there.  Results do not
+ *                  depend on that order.
  * batch == 0 is a no-op.
  */
 size_t qil_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
@@ -287,8 +289,9 @@ int qil_paged_decode_no_alloc(void* out, const void* q, const void* k_cache, con
  *                  QIL_DEBUG checks it
  *   other arguments as qil_paged_decode (workspace sized by
  *   qil_paged_decode_workspace_size).
- * bf16 runs one kernel (plus the ordering and merge passes of the split
- * plan): the split that holds each request's last key reads that key's rows
+ * bf16 runs one kernel (plus, when they apply, the ordering pass for more
+ * than 256 requests and the split merge): the split that holds each
+ * request's last key reads that key's rows
  * from k_new / v_new instead of the pool and stores them at their slot, so
  * the pool row is written and used in the same launch.  fp32 runs the write
  * and the decode as two kernels.  batch == 0 is a no-op.
