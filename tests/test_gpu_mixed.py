@@ -1,9 +1,8 @@
 """qil_paged_attention_mixed: the decode batch and the prefill batch of a step
-in one launch.  Prefill tiles run the same device code with the same tiles
-as qil_paged_prefill, so they must match it bit for bit; decode splits run
-with 8 wavefronts instead of 4 (a different summation order), so they match
-qil_paged_decode within 1e-2 and the oracle within the bf16 tolerance.
-Either batch may be absent."""
+in one launch.  Prefill tiles run the same device code as qil_paged_prefill's
+whole query tiles, and decode splits the same code and split plan as
+qil_paged_decode, so both must match the separate calls bit for bit, and the
+oracle within the bf16 tolerance.  Either batch may be absent."""
 
 import numpy as np
 import pytest
@@ -60,7 +59,7 @@ def test_mixed_step_8b_layer(qil):
     qil.paged_attention_mixed(case.kp, case.vp, float(w.scale), decode=dec, prefill=pre)
     sep_d, sep_p = separate(qil, w, case, dec, pre)
     assert np.array_equal(H.to_bits(pre["out"]), H.to_bits(sep_p))
-    assert np.max(np.abs(H.to_f64(dec["out"]) - H.to_f64(sep_d))) < 1e-2
+    assert np.array_equal(H.to_bits(dec["out"]), H.to_bits(sep_d))
     dsel = list(range(64))
     ref = H.OracleCase(w, case.data, dsel).attention(dsel)
     got = H.to_f64(dec["out"])
@@ -96,4 +95,4 @@ def test_mixed_one_side_only(qil):
     qil.paged_attention_mixed(case.kp, case.vp, float(w.scale), prefill=pre)
     sep_d, sep_p = separate(qil, w, case, dec, pre)
     assert np.array_equal(H.to_bits(pre["out"]), H.to_bits(sep_p))
-    assert np.max(np.abs(H.to_f64(dec["out"]) - H.to_f64(sep_d))) < 1e-2
+    assert np.array_equal(H.to_bits(dec["out"]), H.to_bits(sep_d))
