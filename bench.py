@@ -1158,6 +1158,8 @@ def main():
             "single_launch_us": round(m["single_launch_ms"] * 1e3, 2),
             "us_per_36_layer_step": round(m["layer_ms"] * 1e3 * 36, 1),
             "tokens_per_s_36_layers": round((64 + 2048) / (m["layer_ms"] * 36 * 1e-3), 1),
+            "tokens_per_s_36_layers_single_launch":
+                round((64 + 2048) / (m["single_launch_layer_ms"] * 36 * 1e-3), 1),
             "per_call_timing": "event brackets around each call (pass 1 of timed_steps); a bracket "
                                "includes the dispatch gap a marker puts in front of its kernel",
             "fused_write": {"us": round(m["fused_ms"] * 1e3, 2),
