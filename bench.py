@@ -326,17 +326,24 @@ def gpu_legs(args):
         # the chunk write alone, right after the flush writes (no event marker
         # in front of it): time of (flush, write) minus time of the flush
         write_ms = flushed_kernel_ms(write4, args, flush, stream)
+
+        def append4():
+            # the same step as one call: the prefill kernel stores the new rows
+            qil.paged_prefill_append(x.out, x.q, x.k_new, x.v_new, x.slots, x.kp, x.vp, x.bt, cu,
+                                     x.ctx, maxq, maxk, float(w4.scale), stream=stream)
+        ta = timed_steps([append4], args.steps, args.warmup, flush, stream)
         flops = w4.prefill_flops()
         ntok = int(w4.new_lens.sum())
         res["prefill"] = dict(workload=w4, pre_ms=t["last_ms"], pre_bracket_ms=float(t["mean"][1]),
                               pre_bracket_ms_median=float(t["median"][1]), step_ms=t["step_mean"],
-                              flops=flops, write_ms=write_ms,
+                              append_step_ms=ta["step_mean"], flops=flops, write_ms=write_ms,
                               write_bytes=write_bytes(w4, ntok), write_tokens=ntok)
         print(f"[bench] prefill-varlen: prefill {t['last_ms']*1e3:.1f} us "
               f"({flops / (t['last_ms'] * 1e-3) / 1e12:.1f} TFLOP/s; event bracket "
               f"{t['mean'][1]*1e3:.1f} us); chunk write {ntok} tokens "
-              f"{write_ms*1e3:.1f} us ({write_bytes(w4, ntok) / (write_ms * 1e-3) / 1e9:.0f} GB/s)",
-              flush=True)
+              f"{write_ms*1e3:.1f} us ({write_bytes(w4, ntok) / (write_ms * 1e-3) / 1e9:.0f} GB/s); "
+              f"step as two calls {t['step_mean']*1e3:.1f} us, as one qil_paged_prefill_append "
+              f"call {ta['step_mean']*1e3:.1f} us", flush=True)
         del x
         torch.cuda.empty_cache()
 
@@ -921,7 +928,7 @@ def sources_sha256(files):
 # grid is the bench's one-off pool fill.
 TRAFFIC_KERNELS = {
     "decode-b256": ("decode_mfma_kernel<2>", "largest"),
-    "prefill-varlen": ("prefill_kernel<2, 4>", "largest"),   # 128-row workgroups (short contexts)
+    "prefill-varlen": ("prefill_kernel<2, 4, false>", "largest"),   # 128-row workgroups (short contexts)
     "qkv-proj-8b": ("qkv_proj_kernel<4, false>", "largest"),
     "kv-write-chunk": ("kv_write_kernel<16>", "frequent"),     # the 8,946-token chunk write
     "fused-write-8b": ("kv_write_fused_kernel", "frequent"),   # 2,112 tokens of qkv-proj-8b
@@ -1126,6 +1133,10 @@ def main():
             "event_bracket_us_mean": round(p["pre_bracket_ms"] * 1e3, 2),
             "event_bracket_us_median": round(p["pre_bracket_ms_median"] * 1e3, 2),
             "step_us_mean": round(p["step_ms"] * 1e3, 2),
+            "append_step_us_mean": round(p["append_step_ms"] * 1e3, 2),
+            "step_timing": "step_us_mean: the chunk's qil_kv_write then qil_paged_prefill; "
+                           "append_step_us_mean: the same step as one qil_paged_prefill_append "
+                           "call (event bracket around each step)",
             "traffic": traffic_for("prefill-varlen"),
             "measured_ceiling": res["ceilings"]["mfma_bf16_TFLOP_s"],
             "frac_of_measured": round(tf / res["ceilings"]["mfma_bf16_TFLOP_s"], 4),

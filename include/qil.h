@@ -358,6 +358,44 @@ int qil_paged_prefill(void* out, const void* q, const void* k_cache, const void*
                       void* stream);
 
 /*
+ * qil_paged_prefill_append -- a prefill step's write and attention in one
+ * call: the same result as qil_kv_write(k_new, v_new, slot_mapping) over the
+ * call's total_q new tokens followed by qil_paged_prefill(...)
+ * ("nano-vLLM learning note", prepare_prefill: each new token's slot is the
+ * block-table slot of its position; Attention.forward stores k/v before
+ * attending).
+ *
+ *   k_new, v_new   [total_q] rows of num_kv_heads*head_dim, packed like q by
+ *                  cu_seqlens_q, dtype, token strides in elements
+ *                  (>= num_kv_heads*head_dim, multiples of 8)
+ *   slot_mapping   int32 [total_q]: the slot of each new token's position
+ *                  (block_tables[r][p / page_size] * page_size + p % page_size
+ *                  for position p = context_lens[r] - n_r + i); -1 stores
+ *                  nothing.  The attention reads every new token's K/V from
+ *                  k_new / v_new, so the result equals the two calls whenever
+ *                  the slots follow the block tables (QIL_DEBUG checks the
+ *                  slots' range).
+ *   other arguments as qil_paged_prefill (workspace sized by
+ *   qil_paged_prefill_workspace_size).
+ * bf16 calls of whole query tiles (no split over keys) run one kernel: keys
+ * at a request's new positions are loaded from k_new / v_new, and extra
+ * workgroups at the end of the grid store the new rows into the pools, which
+ * no other workgroup of the launch reads.  fp32 and calls split over keys run
+ * qil_kv_write, then qil_paged_prefill.  batch == 0 or total_q == 0 is a
+ * no-op.
+ */
+int qil_paged_prefill_append(void* out, const void* q, const void* k_new, const void* v_new,
+                             int64_t k_token_stride, int64_t v_token_stride,
+                             const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                             const int32_t* block_tables, int32_t block_table_stride,
+                             const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                             int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                             int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t page_size, int32_t num_pages, float scale,
+                             int32_t dtype, int32_t keys_per_split, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * qil_paged_attention_mixed -- the decode batch and the prefill batch of one
  * step in a single launch over the same KV pool (plus the decode split merge
  * when the decode part has several splits).  The "qwen-engine" README keeps

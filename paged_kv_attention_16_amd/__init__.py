@@ -24,7 +24,7 @@ import os
 __all__ = [
     "QilError", "lib_path", "load", "version", "kv_write", "QKNormRope", "rope_cos_sin",
     "paged_decode", "paged_decode_workspace_size", "paged_decode_no_alloc", "paged_decode_append",
-    "paged_prefill",
+    "paged_prefill", "paged_prefill_append",
     "paged_prefill_workspace_size",
     "paged_attention_mixed",
     "qkv_proj_write", "qkv_proj_workspace_size", "set_debug", "debug_enabled",
@@ -126,6 +126,10 @@ def load(path=None):
     lib.qil_paged_prefill.restype = ctypes.c_int
     lib.qil_paged_prefill.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                       i32, i32, i32, i32, f32, i32, i32, vp, sz, vp]
+    lib.qil_paged_prefill_append.restype = ctypes.c_int
+    lib.qil_paged_prefill_append.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int64, vp,
+                                             vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
+                                             i32, i32, i32, f32, i32, i32, vp, sz, vp]
     lib.qil_paged_prefill_workspace_size.restype = sz
     lib.qil_paged_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     if path is None:
@@ -472,6 +476,43 @@ def paged_prefill(out, q, k_cache, v_cache, block_tables, cu_seqlens_q, context_
         int(block_tables.shape[1]), _ptr(cu_seqlens_q), _ptr(context_lens), batch, total_q,
         int(max_seqlen_q), int(max_context_len), hq, hkv, d, page, num_pages, float(scale),
         _dtype_code(q), int(keys_per_split), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc)
+
+
+def paged_prefill_append(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
+                         cu_seqlens_q, context_lens, max_seqlen_q, max_context_len, scale,
+                         keys_per_split=0, workspace=None, stream=None):
+    """A prefill step's write and attention in one call: k_new, v_new
+    [total_q, Hkv, 128] (or row views with a token stride, as kv_write),
+    slot_mapping int32 [total_q] = slot of each new token's position;
+    otherwise as paged_prefill."""
+    import torch
+    num_pages, hkv, page, d = _pools(k_cache, v_cache)
+    _rows(q, out, "q", "out", k_cache)
+    total_q, hq = int(q.shape[0]), int(q.shape[1])
+    _new_rows(k_new, "k_new", k_cache)
+    _new_rows(v_new, "v_new", k_cache)
+    _need(int(k_new.shape[0]) == total_q and int(v_new.shape[0]) == total_q,
+          "k_new and v_new must hold one row per new token")
+    _i32(slot_mapping, "slot_mapping", k_cache, total_q)
+    _i32(context_lens, "context_lens", k_cache)
+    batch = int(context_lens.shape[0])
+    _i32(cu_seqlens_q, "cu_seqlens_q", k_cache, batch + 1)
+    _i32(block_tables, "block_tables", k_cache, batch, dims=2)
+    _workspace(workspace, k_cache)
+    _on_gpu(k_cache)
+    need = paged_prefill_workspace_size(batch, total_q, int(max_seqlen_q), int(max_context_len),
+                                        hq, hkv, keys_per_split)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load().qil_paged_prefill_append(
+        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _token_stride(k_new, hkv * d),
+        _token_stride(v_new, hkv * d), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_tables), int(block_tables.shape[1]), _ptr(cu_seqlens_q), _ptr(context_lens),
+        batch, total_q, int(max_seqlen_q), int(max_context_len), hq, hkv, d, page, num_pages,
+        float(scale), _dtype_code(q), int(keys_per_split), _ptr(workspace), ws_bytes,
+        _stream(stream))
     _check(rc)
 
 

@@ -886,6 +886,76 @@ int qil_paged_prefill(void* out, const void* q, const void* k_cache, const void*
   return ok();
 }
 
+int qil_paged_prefill_append(void* out, const void* q, const void* k_new, const void* v_new,
+                             int64_t k_token_stride, int64_t v_token_stride,
+                             const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                             const int32_t* block_tables, int32_t block_table_stride,
+                             const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                             int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                             int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t page_size, int32_t num_pages, float scale,
+                             int32_t dtype, int32_t keys_per_split, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  qil::PrefillArgs a;
+  bool empty = false;
+  if (keys_per_split < 0 || keys_per_split % 64 || keys_per_split > kMaxPrefillKeysPerSplit)
+    return fail(QIL_EINVAL, "keys_per_split %d must be 0 or a multiple of 64 up to %d",
+                keys_per_split, kMaxPrefillKeysPerSplit);
+  int rc = prep_prefill(out, q, k_cache, v_cache, block_tables, block_table_stride, cu_seqlens_q,
+                        context_lens, batch, total_q, max_seqlen_q, max_context_len, num_q_heads,
+                        num_kv_heads, head_dim, page_size, num_pages, scale, dtype, a, &empty);
+  if (rc || empty) return rc;
+  if (!k_new || !v_new || !slot_mapping) return fail(QIL_EINVAL, "null pointer argument");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(QIL_EINVAL, "k_new and v_new must be 16-byte aligned");
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (k_token_stride < row || v_token_stride < row || k_token_stride % 8 || v_token_stride % 8)
+    return fail(QIL_EINVAL, "token strides (%lld, %lld) must be >= num_kv_heads*head_dim %lld and "
+                "multiples of 8", (long long)k_token_stride, (long long)v_token_stride,
+                (long long)row);
+  if ((int64_t)num_pages * page_size > INT32_MAX)
+    return fail(QIL_EINVAL, "num_pages*page_size exceeds the int32 slot range");
+  const PrefillPlan plan = plan_prefill(batch, total_q, max_seqlen_q, max_context_len,
+                                        num_q_heads, num_kv_heads, keys_per_split);
+  const size_t need = dtype == QIL_F32 ? 0 : prefill_workspace_bytes(plan, num_kv_heads);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(QIL_EWORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_on()) {
+    const int64_t num_slots = (int64_t)num_pages * page_size;
+    rc = run_checks(s, [&](qil::DebugReport* rep) {
+      hipError_t e = check_prefill_metadata(a, rep, s);
+      if (e == hipSuccess) e = qil::launch_check_slots(slot_mapping, total_q, num_slots, rep, s);
+      return e;
+    });
+    if (rc) return rc;
+  }
+  if (dtype == QIL_BF16 && need == 0) {
+    // one kernel: keys at new positions come from k_new / v_new, and each
+    // query tile's workgroup stores its tokens' rows
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_new_stride = k_token_stride;
+    a.v_new_stride = v_token_stride;
+    a.new_slots = slot_mapping;
+    hipError_t e = qil::launch_prefill_append(a, s);
+    if (e != hipSuccess) return fail(QIL_EHIP, "prefill launch: %s", hipGetErrorString(e));
+    return ok();
+  }
+  // fp32, or a call split over keys: the plain write, then the prefill
+  qil::KvWriteArgs w{k_new, v_new, k_token_stride, v_token_stride, k_cache, v_cache,
+                     slot_mapping, total_q, num_kv_heads, a.log2_page, num_pages,
+                     dtype == QIL_BF16 ? 2 : 4};
+  hipError_t e = qil::launch_kv_write(w, s);
+  if (e != hipSuccess) return fail(QIL_EHIP, "kv_write launch: %s", hipGetErrorString(e));
+  return qil_paged_prefill(out, q, k_cache, v_cache, block_tables, block_table_stride,
+                           cu_seqlens_q, context_lens, batch, total_q, max_seqlen_q,
+                           max_context_len, num_q_heads, num_kv_heads, head_dim, page_size,
+                           num_pages, scale, dtype, keys_per_split, workspace, workspace_bytes,
+                           stream);
+}
+
 int qil_paged_attention_mixed(const qil_decode_batch* decode, const qil_prefill_batch* prefill,
                               const void* k_cache, const void* v_cache, int32_t num_q_heads,
                               int32_t num_kv_heads, int32_t head_dim, int32_t page_size,

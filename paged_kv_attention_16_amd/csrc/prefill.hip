@@ -36,19 +36,27 @@ namespace {
 // step's chunks, one 4,096- or 8,192-token prompt).
 constexpr int kNarrowMaxContext = 2560;
 
-template <int G, int W>
+template <int G, int W, bool APPEND>
 hipError_t launch_gw(const PrefillArgs& a, hipStream_t s) {
   constexpr int TQ = 32 * W / G;
   const int n_qtiles = (a.max_seqlen_q + TQ - 1) / TQ;
   if (n_qtiles == 0 || a.batch == 0) return hipSuccess;
-  dim3 grid(a.num_kv_heads, a.batch, n_qtiles);
-  hipLaunchKernelGGL((prefill_kernel<G, W>), grid, dim3(64 * W), 0, s, a, n_qtiles);
+  int zc = 0;  // copy slices: about two passes of 4 chunks per thread each
+  if (APPEND && a.total_q > 0) {
+    const int64_t chunks = (int64_t)a.total_q * a.num_kv_heads * 32;
+    const int64_t blocks = (chunks + 8 * 64 * W - 1) / (8 * 64 * W);
+    const int64_t slice = (int64_t)a.num_kv_heads * a.batch;
+    zc = (int)std::min<int64_t>((blocks + slice - 1) / slice, 1024);
+  }
+  dim3 grid(a.num_kv_heads, a.batch, n_qtiles + zc);
+  hipLaunchKernelGGL((prefill_kernel<G, W, APPEND>), grid, dim3(64 * W), 0, s, a, n_qtiles);
   return hipGetLastError();
 }
 
-template <int G>
+template <int G, bool APPEND = false>
 hipError_t launch_g(const PrefillArgs& a, hipStream_t s) {
-  return a.max_context_len <= kNarrowMaxContext ? launch_gw<G, 4>(a, s) : launch_gw<G, 8>(a, s);
+  return a.max_context_len <= kNarrowMaxContext ? launch_gw<G, 4, APPEND>(a, s)
+                                                : launch_gw<G, 8, APPEND>(a, s);
 }
 
 // Key tiles of query tile `tile` of request r (0 when the tile has no rows),
@@ -290,6 +298,19 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     case 5: return launch_g<5>(a, s);
     case 8: return launch_g<8>(a, s);
     case 16: return launch_g<16>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_prefill_append(const PrefillArgs& a, hipStream_t s) {
+  if (a.k_new == nullptr || a.v_new == nullptr || a.new_slots == nullptr) return hipErrorInvalidValue;
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_g<1, true>(a, s);
+    case 2: return launch_g<2, true>(a, s);
+    case 4: return launch_g<4, true>(a, s);
+    case 5: return launch_g<5, true>(a, s);
+    case 8: return launch_g<8, true>(a, s);
+    case 16: return launch_g<16, true>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -122,7 +122,10 @@ typedef char PrefillLds[2][2][kBN * 256];
 // reference maximum (log2 domain) and weight sum to part_ml (rows
 // ml_row_stride pairs apart).  Every thread of the workgroup of W
 // wavefronts (32 W query rows) calls it; `smem` is the workgroup's LDS.
-template <int G, int W = kWaves>
+// APPEND (whole tiles only): keys at the request's new positions come from
+// a.k_new / a.v_new instead of the pools (other workgroups of the launch
+// store those rows into the pools meanwhile).
+template <int G, int W = kWaves, bool APPEND = false>
 __device__ __forceinline__ void prefill_range(const PrefillArgs& a, int g, int r, int tile,
                                               int kt_begin, int kt_end, float* part_o,
                                               float* part_ml, int ml_row_stride, PrefillLds& smem) {
@@ -219,8 +222,15 @@ __device__ __forceinline__ void prefill_range(const PrefillArgs& a, int g, int r
       lds_char* kdst = (lds_char*)&smem[buf][0][0] + (kRowsPerWave * w + 4 * m2) * 256;
       lds_char* vdst = (lds_char*)&smem[buf][1][0] + (kRowsPerWave * w + 4 * m2) * 256;
       if (key < L) {
-        lds_dma16(kpool + grow * 256 + 16 * k_chunk(row, lpc), kdst);
-        lds_dma16(vpool + grow * 256 + 16 * v_chunk(row, lpc), vdst);
+        const char* ksrc = kpool + grow * 256;
+        const char* vsrc = vpool + grow * 256;
+        if (APPEND && key >= prefix) {  // a new token: its row is an input of this call
+          const int64_t t = (int64_t)q0 + (key - prefix);
+          ksrc = static_cast<const char*>(a.k_new) + (t * a.k_new_stride + (int64_t)g * kHeadDim) * 2;
+          vsrc = static_cast<const char*>(a.v_new) + (t * a.v_new_stride + (int64_t)g * kHeadDim) * 2;
+        }
+        lds_dma16(ksrc + 16 * k_chunk(row, lpc), kdst);
+        lds_dma16(vsrc + 16 * v_chunk(row, lpc), vdst);
       }
     }
   };
@@ -435,12 +445,61 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int n_qtiles,
   prefill_range<G, W>(a, g, r, n_qtiles - 1 - z, 0, 1 << 30, nullptr, nullptr, 0, smem);
 }
 
+// Copy workgroup `cb` of `ncb`: stores the new tokens' K and V rows into
+// their pool slots, 16-byte chunks (32 per token and KV head: 16 of K, 16 of
+// V), four per thread in flight, the workgroups striding over the flat chunk
+// index.  A slot of -1 or past the pools stores nothing.
+template <int W>
+__device__ __forceinline__ void append_rows(const PrefillArgs& a, int cb, int ncb) {
+  constexpr int T = 64 * W;
+  const int64_t nchunks = (int64_t)a.total_q * a.num_kv_heads * 32;
+  const int pmask = (1 << a.log2_page) - 1;
+  char* kpool = static_cast<char*>(const_cast<void*>(a.k_cache));  // writable for this entry point
+  char* vpool = static_cast<char*>(const_cast<void*>(a.v_cache));
+  for (int64_t base = (int64_t)cb * 4 * T; base < nchunks; base += (int64_t)ncb * 4 * T) {
+    uint4 val[4];
+    char* dst[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t idx = base + u * T + threadIdx.x;
+      dst[u] = nullptr;
+      if (idx < nchunks) {
+        const int c = (int)(idx & 31);
+        const int64_t th = idx >> 5;
+        const int h = (int)(th % a.num_kv_heads);
+        const int64_t t = th / a.num_kv_heads;
+        const bool isv = c >= 16;
+        const int32_t slot = a.new_slots[t];
+        const int64_t page = slot >> a.log2_page;
+        val[u] = *reinterpret_cast<const uint4*>(
+            static_cast<const char*>(isv ? a.v_new : a.k_new) +
+            (t * (isv ? a.v_new_stride : a.k_new_stride) + (int64_t)h * kHeadDim) * 2 + 16 * (c & 15));
+        if (slot >= 0 && page < a.num_pages)
+          dst[u] = (isv ? vpool : kpool) +
+                   (((page * a.num_kv_heads + h) << a.log2_page) + (slot & pmask)) * 256 + 16 * (c & 15);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (dst[u] != nullptr) *reinterpret_cast<uint4*>(dst[u]) = val[u];
+  }
+}
+
 // W = 8: one workgroup per CU; W = 4: two per CU (two wavefronts per SIMD
-// either way, at most 256 registers each).
-template <int G, int W>
+// either way, at most 256 registers each).  With APPEND the grid has extra
+// z-slices past n_qtiles whose workgroups copy the new rows into the pools;
+// the dispatcher hands them out last, to CUs the longest tiles leave idle.
+template <int G, int W, bool APPEND = false>
 __global__ __launch_bounds__(64 * W, 2) void prefill_kernel(PrefillArgs a, int n_qtiles) {
   __shared__ __attribute__((aligned(1024))) PrefillLds smem;
-  prefill_tile<G, W>(a, n_qtiles, blockIdx.x, blockIdx.y, blockIdx.z, smem);
+  if (APPEND && (int)blockIdx.z >= n_qtiles) {
+    const int slice = gridDim.x * gridDim.y;
+    append_rows<W>(a, ((int)blockIdx.z - n_qtiles) * slice + blockIdx.y * gridDim.x + blockIdx.x,
+                   ((int)gridDim.z - n_qtiles) * slice);
+    return;
+  }
+  prefill_range<G, W, APPEND>(a, blockIdx.x, blockIdx.y, n_qtiles - 1 - (int)blockIdx.z, 0, 1 << 30,
+                              nullptr, nullptr, 0, smem);
 }
 
 }  // namespace

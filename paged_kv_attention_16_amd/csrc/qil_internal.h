@@ -143,6 +143,16 @@ struct PrefillArgs {
   int32_t log2_page;
   int32_t num_pages;
   float scale;
+  // Append (bf16 whole query tiles only; null = plain prefill): the new
+  // tokens' K/V rows k_new/v_new [total_q][Hkv][128] (token strides in
+  // elements).  Keys at a request's new positions are read from these rows
+  // instead of the pool, and the workgroup that owns a query tile stores its
+  // tokens' rows of its KV head at new_slots (-1 or out of range: skipped).
+  const void* k_new;
+  const void* v_new;
+  int64_t k_new_stride;
+  int64_t v_new_stride;
+  const int32_t* new_slots;
 };
 
 // Split plan of a prefill call.  A query tile whose key range spans more
@@ -169,6 +179,8 @@ constexpr int kMaxPieces = 32;         // pieces per query tile
 constexpr int kMaxPlanEntries = 4096;  // batch * n_qtiles of a split call
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+// whole query tiles with the append fields set (a.k_new non-null)
+hipError_t launch_prefill_append(const PrefillArgs& a, hipStream_t s);
 // plan, pieces and merge of a split call
 hipError_t launch_prefill_split(const PrefillArgs& a, const PrefillSplit& sp, hipStream_t s);
 

@@ -179,6 +179,37 @@ def test_prefill_validation(lib):
     assert pre(lib, kps=64 * 1024) == EINVAL        # above 65472
 
 
+def pre_app(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, kn=FAKE, vn=FAKE, ks=1024, vs=1024, slots=FAKE, kc=FAKE, vc=FAKE,
+             bt=FAKE, bts=200, cu=FAKE, ctx=FAKE, B=8, T=8000, maxq=2048, maxL=2560, hq=16,
+             hkv=8, d=128, page=16, pages=900, scale=0.088, dtype=1, kps=0, ws=None, wsb=0)
+    a.update(kw)
+    return lib.qil_paged_prefill_append(
+        a["out"], a["q"], a["kn"], a["vn"], a["ks"], a["vs"], a["slots"], a["kc"], a["vc"],
+        a["bt"], a["bts"], a["cu"], a["ctx"], a["B"], a["T"], a["maxq"], a["maxL"], a["hq"],
+        a["hkv"], a["d"], a["page"], a["pages"], a["scale"], a["dtype"], a["kps"], a["ws"],
+        a["wsb"], None)
+
+
+def test_prefill_append_validation(lib):
+    assert pre_app(lib, B=0) == 0
+    assert pre_app(lib, T=0) == 0
+    # the prefill's own checks come first
+    assert pre_app(lib, maxq=9000) == EINVAL
+    assert pre_app(lib, cu=None) == EINVAL
+    assert pre_app(lib, dtype=2) == EUNSUP
+    assert pre_app(lib, kps=100) == EINVAL
+    # then the new rows and their slots
+    assert pre_app(lib, kn=None) == EINVAL
+    assert pre_app(lib, slots=None) == EINVAL
+    assert pre_app(lib, vn=FAKE + 8) == EINVAL       # misaligned
+    assert pre_app(lib, ks=1000) == EINVAL           # stride below a row
+    assert pre_app(lib, vs=1028) == EINVAL           # stride not a multiple of 8
+    # a call split over keys needs its workspace, as qil_paged_prefill
+    assert pre_app(lib, B=1, T=512, maxq=512, maxL=8192, hq=32, hkv=8, bts=512) == EWS
+    assert len(lib.qil_last_error()) > 0
+
+
 def test_prefill_split_workspace(lib):
     ws = lib.qil_paged_prefill_workspace_size
     # 8 chunks of up to 2,048 tokens: 568 query tiles x KV heads, never split automatically
