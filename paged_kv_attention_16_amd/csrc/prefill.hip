@@ -265,8 +265,8 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArg
   if (!live) return;
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
   uint2 st;
-  st.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  st.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  st.x = cvt_pk_bf16(acc[0] * inv, acc[1] * inv);
+  st.y = cvt_pk_bf16(acc[2] * inv, acc[3] * inv);
   uint16_t* out = static_cast<uint16_t*>(a.out) +
                   ((int64_t)(q0 + t0 + tok) * a.num_q_heads + g * G + hh) * kHeadDim;
   *reinterpret_cast<uint2*>(out + 4 * hl) = st;

@@ -430,8 +430,8 @@ __device__ __forceinline__ void prefill_range(const PrefillArgs& a, int g, int r
     for (int q4 = 0; q4 < 4; ++q4) {
       const int d0 = 32 * db + 8 * q4 + 4 * hf;
       uint2 st;
-      st.x = pack_bf16x2(oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv);
-      st.y = pack_bf16x2(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv);
+      st.x = cvt_pk_bf16(oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv);
+      st.y = cvt_pk_bf16(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv);
       *reinterpret_cast<uint2*>(orow + d0) = st;
     }
   }
