@@ -117,12 +117,15 @@ def small_case(seed, hidden, hq, hkv, ntok, page=16, drop=()):
     (512, 32, 8, 1500, 0),   # 256-token workgroups (one round of 144), ragged last tile
     (4096, 32, 8, 64, 0),    # a decode step of the 8B shape: 10 splits of the hidden dimension
     (4096, 32, 8, 16, 0),    # 16 tokens, 10 splits
+    (1088, 40, 8, 1, 64),    # one token: split path, 17 64-column slices
+    (192, 32, 8, 33, 8),     # 33 tokens over 3 slices, a token stride
     (2048, 16, 8, 300, 8),   # 0.6B-like heads, 3 token tiles, split path with a token stride
 ])
 def test_small_shapes(qil, hidden, hq, hkv, ntok, x_pad):
     print(f"qkv_proj hidden={hidden} hq={hq} hkv={hkv} tokens={ntok}", flush=True)
+    drop = tuple(sorted({0, ntok - 1, ntok // 2}))[:ntok - 1]  # at least one token stays
     x_bits, w_bits, npg, slots, pos, qw, kw, table = small_case(
-        hidden + hq + ntok, hidden, hq, hkv, ntok, drop=(0, ntok - 1, ntok // 2))
+        hidden + hq + ntok, hidden, hq, hkv, ntok, drop=drop)
     check_case(qil, x_bits, w_bits, hq, hkv, 16, npg, slots, pos, qw, kw, 1e-6, table, x_pad)
 
 
