@@ -82,6 +82,26 @@ def test_prefill_checks():
     expect(lambda: run(), "must be GPU tensors")
 
 
+def test_prefill_append_checks():
+    kp, vp = pools()
+
+    def run(**kw):
+        a = dict(out=torch.zeros(10, 4, 128, dtype=BF), q=torch.zeros(10, 4, 128, dtype=BF),
+                 k_new=torch.zeros(10, 2, 128, dtype=BF), v_new=torch.zeros(10, 2, 128, dtype=BF),
+                 slots=torch.zeros(10, dtype=I32), block_tables=torch.zeros(2, 4, dtype=I32),
+                 cu=torch.tensor([0, 4, 10], dtype=I32), ctx=torch.tensor([8, 6], dtype=I32))
+        a.update(kw)
+        qil.paged_prefill_append(a["out"], a["q"], a["k_new"], a["v_new"], a["slots"], kp, vp,
+                                 a["block_tables"], a["cu"], a["ctx"], 6, 8, 0.088)
+    expect(lambda: run(k_new=torch.zeros(10, 2, 128, dtype=F32)), "k_new has dtype")
+    expect(lambda: run(v_new=torch.zeros(9, 2, 128, dtype=BF)), "one row per new token")
+    expect(lambda: run(slots=torch.zeros(10, dtype=torch.int64)), "slot_mapping has dtype")
+    expect(lambda: run(slots=torch.zeros(9, dtype=I32)), "slot_mapping has 9 entries")
+    expect(lambda: run(cu=torch.tensor([0, 4, 10], dtype=torch.int64)), "cu_seqlens_q has dtype")
+    expect(lambda: run(out=torch.zeros(10, 4, 128, dtype=F32)), "out has dtype")
+    expect(lambda: run(), "must be GPU tensors")
+
+
 def test_kv_write_checks():
     kp, vp = pools()
     k = torch.zeros(5, 2, 128, dtype=BF)
